@@ -1,0 +1,212 @@
+/*
+ * vdit_attn — non-causal multi-head attention for video diffusion transformers
+ * on AMD Instinct MI355X (gfx950), one device's share of the heads.
+ *
+ * The operation. In a video DiT split across devices with Ulysses sequence
+ * parallelism, an all-to-all before every attention layer hands each device
+ * the whole spatio-temporal token sequence for a slice of the heads (fal.ai,
+ * "Generate video with WAN 2.2 across four GPUs", section "Splitting one
+ * generation across four GPUs": four GPUs each attend over the full sequence
+ * for 10 of the 40 heads). The attention itself is non-causal and may take a
+ * key mask (ComfyUI issue "MultiGPU Work Units": the WAN forward pass calls
+ * sageattn with attn_mask and is_causal=False). This library computes, for
+ * every selected head h and query token i,
+ *
+ *     out[i, h - head_begin, :] = sum_j w_ij v[j, h, :],
+ *     w_ij = exp(s_ij - max_j s_ij) / sum_j exp(s_ij - max_j s_ij),
+ *     s_ij = scale * <q'[i, h, :], k'[j, h, :]>,   j < key_len,
+ *
+ * where q' and k' are q and k, optionally rotated by a 3D rotary position
+ * embedding over a (T, H, W) latent grid (below). Sequence parallelism is
+ * numerically faithful to a single device (LTX-2 "Multi-GPU Inference",
+ * section "Capabilities"); here a head share computes bit-for-bit the same
+ * values as the same heads inside an all-heads call.
+ *
+ * 3D RoPE reading (the pages name no formula): token n of the grid, w fastest,
+ * sits at t = n / (H*W), y = (n / W) % H, x = n % W. The head dimension is cut
+ * into three consecutive bands of widths (rope_dim_t, rope_dim_h, rope_dim_w);
+ * band b rotates its adjacent pairs (2i, 2i+1) by theta = pos_b * base^(-2i/D_b).
+ * cos/sin are tabulated on the host in double precision and rounded to float;
+ * the rotation runs in float (a*c - b*s, a*s + b*c, each as one fused
+ * multiply-add) and the result is rounded to bfloat16 before the products.
+ *
+ * Numerics: q.k products in bfloat16 with float32 accumulation; softmax in
+ * float32 with a running maximum and sum (online softmax); the weights are
+ * rounded to float16 and v is converted once to float16 for the weighted sum
+ * (float32 accumulation); the output is rounded to bfloat16 (nearest even).
+ * v values must lie within the float16 range (|v| <= 65504).
+ *
+ * Conventions for every entry point:
+ *   - all tensors live in device memory owned by the caller; the library
+ *     never frees or keeps them past the call;
+ *   - pointers passed to compute calls must be 16-byte aligned;
+ *   - calls taking `hip_stream` (a hipStream_t; NULL = default stream) only
+ *     enqueue work on that stream and never synchronise the host;
+ *   - errors come back as vdit_status_t values, never as exceptions or aborts;
+ *     a shape or argument error is reported before anything is enqueued;
+ *   - the handle is immutable after create: calls on one handle may run on
+ *     different streams concurrently if their workspaces are distinct;
+ *   - compute calls must run with the device current that was current at create.
+ */
+#ifndef VDIT_ATTN_H
+#define VDIT_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct vdit_attn* vdit_attn_t;
+
+typedef enum {
+  VDIT_OK = 0,
+  VDIT_ERR_INVALID_ARG = 1,    /* NULL pointer, bad shape, bad head range, bad key_len, aliasing */
+  VDIT_ERR_UNSUPPORTED = 2,    /* valid request outside what the kernels implement (e.g. d not 64/128) */
+  VDIT_ERR_ALIGNMENT = 3,      /* a device pointer is not 16-byte aligned */
+  VDIT_ERR_OUT_OF_MEMORY = 4,  /* the small create-time device tables could not be allocated */
+  VDIT_ERR_DEVICE = 5,         /* a HIP call or kernel launch failed, or the wrong device is current */
+  VDIT_ERR_WORKSPACE = 6       /* workspace NULL or smaller than vdit_attn_workspace_bytes() */
+} vdit_status_t;
+
+typedef enum {
+  VDIT_LAYOUT_NHD = 0,  /* q [nq, Ht, d], k and v [nk, Ht, d]; bfloat16, contiguous */
+  VDIT_LAYOUT_N3HD = 1  /* one packed tensor [n, 3, Ht, d] bfloat16 (index 0 = q, 1 = k, 2 = v); nq == nk */
+} vdit_layout_t;
+
+/*
+ * Problem description, fixed at create. Sizes in elements.
+ *   nq, nk          query and key tokens (self-attention: equal; text cross-attention:
+ *                   nk = text length)
+ *   heads_total     Ht, heads present in the tensors (e.g. 40)
+ *   head_dim        d, 64 or 128
+ *   layout          vdit_layout_t
+ *   head_begin/count  selected heads [head_begin, head_begin + head_count) of Ht; the
+ *                   output holds only these, in order
+ *   scale           softmax scale; <= 0 selects 1/sqrt(d); NaN or inf is rejected
+ *   use_key_mask    0: all nk keys; 1: only keys j < key_len (key_len given per call)
+ *   use_rope        1: rotate q and k by the 3D RoPE above (requires nq == nk)
+ *   grid_t/h/w      latent grid, grid_t * grid_h * grid_w == nq (used iff use_rope)
+ *   rope_dim_t/h/w  band widths, each even and > 0, summing to d (used iff use_rope)
+ *   rope_base       base of the frequencies, > 0 and finite (used iff use_rope)
+ */
+typedef struct {
+  int32_t nq;
+  int32_t nk;
+  int32_t heads_total;
+  int32_t head_dim;
+  int32_t layout;
+  int32_t head_begin;
+  int32_t head_count;
+  float scale;
+  int32_t use_key_mask;
+  int32_t use_rope;
+  int32_t grid_t, grid_h, grid_w;
+  int32_t rope_dim_t, rope_dim_h, rope_dim_w;
+  double rope_base;
+} vdit_attn_desc_t;
+
+/*
+ * Head share of one rank under Ulysses sequence parallelism of `degree` ranks:
+ * heads [rank * Ht / degree, (rank + 1) * Ht / degree). fal.ai "Generate video
+ * with WAN 2.2 across four GPUs", sections "Splitting one generation across
+ * four GPUs" (10 of 40 heads per GPU at degree 4) and "Tuning cost and GPU
+ * count" (the degree must divide the head count; FastVideo "Pair two NVIDIA DGX
+ * Sparks", section "What we are not claiming", states the same for sp_size).
+ * Host only. INVALID_ARG if degree <= 0, heads_total <= 0, heads_total % degree
+ * != 0, rank outside [0, degree), or an output pointer is NULL.
+ */
+vdit_status_t vdit_attn_ulysses_heads(int32_t heads_total, int32_t degree, int32_t rank,
+                                      int32_t* head_begin, int32_t* head_count);
+
+/*
+ * Validate `desc` and build a plan: tile shapes and launch grid are fixed here
+ * for the shape, with no tuning at run time (the fal.ai page, section "Converting
+ * once, starting the runner, warming up", notes that per-shape autotuning costs
+ * a cold request tens of seconds). With use_rope, the cos/sin tables are built in
+ * double precision, rounded to float and copied to the current device (the only
+ * device memory the handle owns). Shape errors return INVALID_ARG or UNSUPPORTED
+ * without touching the device. On success *out receives a handle that the caller
+ * releases with vdit_attn_destroy.
+ */
+vdit_status_t vdit_attn_create(const vdit_attn_desc_t* desc, vdit_attn_t* out);
+
+/* Release a handle and its tables. NULL is accepted (VDIT_OK). */
+vdit_status_t vdit_attn_destroy(vdit_attn_t h);
+
+/*
+ * Bytes of caller-provided device workspace that prepare/attend/fwd need for the
+ * largest key length of this plan: v transposed to float16 per head
+ * ([head_count][ceil(nk/64)*64][d], 2 bytes) and, with use_rope, the rotated keys
+ * per head (same shape, bfloat16). Host only.
+ */
+vdit_status_t vdit_attn_workspace_bytes(vdit_attn_t h, size_t* bytes);
+
+/*
+ * The whole forward pass on `hip_stream`: vdit_attn_prepare then vdit_attn_attend.
+ *   q, k, v    NHD: q [nq, Ht, d], k and v [nk, Ht, d] (bfloat16).
+ *              N3HD: q is the packed [n, 3, Ht, d] tensor; k and v must be NULL.
+ *   key_len    used iff use_key_mask: 1 <= key_len <= nk (keys j >= key_len are
+ *              excluded; their k and v contents are never read); otherwise ignored.
+ *   out        bfloat16 [nq, head_count, d], contiguous; must not overlap the inputs
+ *              or the workspace.
+ *   workspace  >= vdit_attn_workspace_bytes() bytes of device memory; its contents
+ *              are overwritten.
+ */
+vdit_status_t vdit_attn_fwd(vdit_attn_t h, const void* q, const void* k, const void* v,
+                            int32_t key_len, void* out, void* workspace, size_t workspace_bytes,
+                            void* hip_stream);
+
+/*
+ * First stage of fwd: writes v (heads of the share, keys < key_len) transposed
+ * and converted to float16 into the workspace, zero-filled up to the next
+ * multiple of 64 keys; with use_rope also the rotated keys (bfloat16). Arguments
+ * as for fwd (q is read only for the N3HD layout, where it is the packed tensor).
+ */
+vdit_status_t vdit_attn_prepare(vdit_attn_t h, const void* q, const void* k, const void* v,
+                                int32_t key_len, void* workspace, size_t workspace_bytes,
+                                void* hip_stream);
+
+/*
+ * Second stage of fwd: the attention kernel proper. Reads q (and, without
+ * RoPE, k) from the inputs and the prepared workspace from vdit_attn_prepare,
+ * which must have been enqueued before it with the same inputs and key_len.
+ * Arguments as for fwd.
+ */
+vdit_status_t vdit_attn_attend(vdit_attn_t h, const void* q, const void* k, const void* v,
+                               int32_t key_len, void* out, void* workspace, size_t workspace_bytes,
+                               void* hip_stream);
+
+/*
+ * Layout change for the Ulysses exchange (fal.ai page, section "Splitting one
+ * generation across four GPUs": tokens are traded for heads at every attention
+ * layer; LTX-2 "Multi-GPU Inference", section "Requirements", names a dedicated
+ * all-to-all kernel for it). pack: src [n, Ht, d] -> dst [groups, n, Ht/groups, d],
+ * i.e. dst[g, t, j, :] = src[t, g * Ht/groups + j, :]. unpack is the inverse.
+ * Pure 2-byte-element permutation (bit-exact). INVALID_ARG if groups does not
+ * divide Ht, a size is <= 0, a pointer is NULL or the buffers overlap; ALIGNMENT
+ * if a pointer is not 16-byte aligned or d * 2 is not a multiple of 16.
+ */
+vdit_status_t vdit_pack_heads(const void* src, void* dst, int32_t n, int32_t heads_total,
+                              int32_t head_dim, int32_t groups, void* hip_stream);
+vdit_status_t vdit_unpack_heads(const void* src, void* dst, int32_t n, int32_t heads_total,
+                                int32_t head_dim, int32_t groups, void* hip_stream);
+
+/*
+ * Debug probe of the RoPE index mapping the kernels use: for every query token n
+ * in [0, nq) and pair p in [0, d/2), writes five int32 values
+ * idx_out[(n * d/2 + p) * 5 + {0..4}] = (t, y, x, band, i), computed by the same
+ * device code that rotates q and k. idx_out: device memory, nq * d/2 * 5 int32.
+ * INVALID_ARG if the handle was created without use_rope or idx_out is NULL.
+ */
+vdit_status_t vdit_attn_rope_probe(vdit_attn_t h, int32_t* idx_out, void* hip_stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* vdit_status_string(vdit_status_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VDIT_ATTN_H */

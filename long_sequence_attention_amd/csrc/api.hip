@@ -1,0 +1,399 @@
+// C-ABI entry points: validation, plan, RoPE tables and launches.
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <unordered_set>
+#include <vector>
+
+#include "common.hpp"
+#include "vdit_attn.h"
+
+struct vdit_attn {
+  vdit_attn_desc_t desc;
+  float scale;
+  float c;             // scale * log2(e)
+  int device;
+  int64_t nk_pad;      // keys rounded up to the key tile
+  size_t ws_vt_off, ws_vt_bytes;
+  size_t ws_kr_off, ws_kr_bytes;
+  size_t ws_total;
+  float2* rope_tab;    // device (cos, sin) table, or nullptr
+  vdit::RopeGeom geom;
+};
+
+namespace {
+
+// Live handles, so that a stale or foreign pointer (e.g. a second destroy) is
+// rejected without touching freed memory.
+std::mutex g_live_mu;
+std::unordered_set<const vdit_attn*>& live_handles() {
+  static std::unordered_set<const vdit_attn*> s;
+  return s;
+}
+
+bool is_live(const vdit_attn* h) {
+  if (!h) return false;
+  std::lock_guard<std::mutex> lk(g_live_mu);
+  return live_handles().count(h) != 0;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+vdit_status_t validate_desc(const vdit_attn_desc_t& d) {
+  if (d.head_dim != 64 && d.head_dim != 128) return VDIT_ERR_UNSUPPORTED;
+  if (d.nq < 1 || d.nk < 1 || d.heads_total < 1) return VDIT_ERR_INVALID_ARG;
+  if (d.layout != VDIT_LAYOUT_NHD && d.layout != VDIT_LAYOUT_N3HD) return VDIT_ERR_INVALID_ARG;
+  if (d.layout == VDIT_LAYOUT_N3HD && d.nq != d.nk) return VDIT_ERR_INVALID_ARG;
+  if (d.head_begin < 0 || d.head_count < 1 || (int64_t)d.head_begin + d.head_count > d.heads_total)
+    return VDIT_ERR_INVALID_ARG;
+  if (d.head_count > 65535) return VDIT_ERR_UNSUPPORTED;
+  if (std::isnan(d.scale) || std::isinf(d.scale)) return VDIT_ERR_INVALID_ARG;
+  if (d.use_key_mask != 0 && d.use_key_mask != 1) return VDIT_ERR_INVALID_ARG;
+  if (d.use_rope != 0 && d.use_rope != 1) return VDIT_ERR_INVALID_ARG;
+  // element offsets are 64-bit in the kernels; keep every tensor below 2^60 elements
+  const int64_t row = (int64_t)d.heads_total * d.head_dim * (d.layout == VDIT_LAYOUT_N3HD ? 3 : 1);
+  const int64_t nmax = d.nq > d.nk ? d.nq : d.nk;
+  if (row > (int64_t(1) << 40) || nmax * row > (int64_t(1) << 60)) return VDIT_ERR_INVALID_ARG;
+  if (d.use_rope) {
+    if (d.nq != d.nk) return VDIT_ERR_INVALID_ARG;
+    if (d.grid_t < 1 || d.grid_h < 1 || d.grid_w < 1) return VDIT_ERR_INVALID_ARG;
+    if ((int64_t)d.grid_t * d.grid_h * d.grid_w != d.nq) return VDIT_ERR_INVALID_ARG;
+    const int32_t bt = d.rope_dim_t, bh = d.rope_dim_h, bw = d.rope_dim_w;
+    if (bt < 2 || bh < 2 || bw < 2 || (bt | bh | bw) & 1) return VDIT_ERR_INVALID_ARG;
+    if ((int64_t)bt + bh + bw != d.head_dim) return VDIT_ERR_INVALID_ARG;
+    if (!(d.rope_base > 0.0) || std::isinf(d.rope_base)) return VDIT_ERR_INVALID_ARG;
+  }
+  return VDIT_OK;
+}
+
+// cos/sin of theta = pos * base^(-2i/D) for every band position and pair index,
+// computed in double precision and rounded to float.
+void build_rope_table(const vdit_attn_desc_t& d, std::vector<float2>& tab, vdit::RopeGeom& g) {
+  const int32_t dims[3] = {d.rope_dim_t, d.rope_dim_h, d.rope_dim_w};
+  const int32_t npos[3] = {d.grid_t, d.grid_h, d.grid_w};
+  int32_t off[3];
+  int64_t total = 0;
+  for (int b = 0; b < 3; ++b) {
+    off[b] = (int32_t)total;
+    total += (int64_t)npos[b] * (dims[b] / 2);
+  }
+  tab.assign((size_t)total, float2{0.f, 0.f});
+  for (int b = 0; b < 3; ++b) {
+    const int32_t half = dims[b] / 2;
+    for (int32_t pos = 0; pos < npos[b]; ++pos)
+      for (int32_t i = 0; i < half; ++i) {
+        const double inv_freq = std::pow(d.rope_base, -2.0 * (double)i / (double)dims[b]);
+        const double theta = (double)pos * inv_freq;
+        tab[(size_t)off[b] + (size_t)pos * half + i] = float2{(float)std::cos(theta), (float)std::sin(theta)};
+      }
+  }
+  g.grid_h = d.grid_h;
+  g.grid_w = d.grid_w;
+  g.half_t = dims[0] / 2;
+  g.half_h = dims[1] / 2;
+  g.half_w = dims[2] / 2;
+  g.pair_h = g.half_t;
+  g.pair_w = g.half_t + g.half_h;
+  g.off_h = off[1];
+  g.off_w = off[2];
+}
+
+struct Inputs {
+  const __bf16 *q, *k, *v;  // pointing at head_begin, token 0
+  int64_t q_row, kv_row;
+  size_t q_bytes, k_bytes, v_bytes;  // extents for the overlap checks
+  const void *q_base, *k_base, *v_base;
+};
+
+vdit_status_t resolve_inputs(const vdit_attn& h, const void* q, const void* k, const void* v, Inputs& in) {
+  const vdit_attn_desc_t& d = h.desc;
+  const int64_t hd = (int64_t)d.heads_total * d.head_dim;
+  if (!q) return VDIT_ERR_INVALID_ARG;
+  if (d.layout == VDIT_LAYOUT_N3HD) {
+    if (k || v) return VDIT_ERR_INVALID_ARG;
+    if (!aligned16(q)) return VDIT_ERR_ALIGNMENT;
+    const __bf16* base = static_cast<const __bf16*>(q) + (int64_t)d.head_begin * d.head_dim;
+    in.q = base;
+    in.k = base + hd;
+    in.v = base + 2 * hd;
+    in.q_row = in.kv_row = 3 * hd;
+    in.q_bytes = (size_t)d.nq * 3 * hd * 2;
+    in.k_bytes = in.v_bytes = 0;
+    in.q_base = q;
+    in.k_base = in.v_base = nullptr;
+  } else {
+    if (!k || !v) return VDIT_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return VDIT_ERR_ALIGNMENT;
+    const int64_t off = (int64_t)d.head_begin * d.head_dim;
+    in.q = static_cast<const __bf16*>(q) + off;
+    in.k = static_cast<const __bf16*>(k) + off;
+    in.v = static_cast<const __bf16*>(v) + off;
+    in.q_row = in.kv_row = hd;
+    in.q_bytes = (size_t)d.nq * hd * 2;
+    in.k_bytes = in.v_bytes = (size_t)d.nk * hd * 2;
+    in.q_base = q;
+    in.k_base = k;
+    in.v_base = v;
+  }
+  return VDIT_OK;
+}
+
+vdit_status_t check_call(const vdit_attn& h, int32_t key_len, void* workspace, size_t ws_bytes, int32_t& kv_len) {
+  const vdit_attn_desc_t& d = h.desc;
+  if (d.use_key_mask) {
+    if (key_len < 1 || key_len > d.nk) return VDIT_ERR_INVALID_ARG;
+    kv_len = key_len;
+  } else {
+    kv_len = d.nk;
+  }
+  if (!workspace || ws_bytes < h.ws_total) return VDIT_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return VDIT_ERR_ALIGNMENT;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != h.device) return VDIT_ERR_DEVICE;
+  return VDIT_OK;
+}
+
+vdit_status_t do_prepare(const vdit_attn& h, const Inputs& in, int32_t kv_len, void* ws, hipStream_t s) {
+  const vdit_attn_desc_t& d = h.desc;
+  vdit::PrepArgs a{};
+  a.k = in.k;
+  a.v = in.v;
+  a.kv_row = in.kv_row;
+  a.kv_head = d.head_dim;
+  a.vt = reinterpret_cast<_Float16*>(static_cast<char*>(ws) + h.ws_vt_off);
+  a.vt_head = h.nk_pad * d.head_dim;
+  a.kr = d.use_rope ? reinterpret_cast<__bf16*>(static_cast<char*>(ws) + h.ws_kr_off) : nullptr;
+  a.kr_head = h.nk_pad * d.head_dim;
+  a.kv_len = kv_len;
+  a.n_ktiles = (kv_len + vdit::kBlockN - 1) / vdit::kBlockN;
+  a.hc = d.head_count;
+  a.rope = h.geom;
+  if (vdit::launch_prepare(a, d.head_dim, d.use_rope != 0, s) != hipSuccess) return VDIT_ERR_DEVICE;
+  return VDIT_OK;
+}
+
+vdit_status_t do_attend(const vdit_attn& h, const Inputs& in, int32_t kv_len, void* out, void* ws, hipStream_t s) {
+  const vdit_attn_desc_t& d = h.desc;
+  vdit::AttnArgs a{};
+  a.q = in.q;
+  a.q_row = in.q_row;
+  a.q_head = d.head_dim;
+  if (d.use_rope) {
+    a.k = reinterpret_cast<const __bf16*>(static_cast<const char*>(ws) + h.ws_kr_off);
+    a.k_row = d.head_dim;
+    a.k_head = h.nk_pad * d.head_dim;
+  } else {
+    a.k = in.k;
+    a.k_row = in.kv_row;
+    a.k_head = d.head_dim;
+  }
+  a.vt = reinterpret_cast<const _Float16*>(static_cast<const char*>(ws) + h.ws_vt_off);
+  a.vt_head = h.nk_pad * d.head_dim;
+  a.out = static_cast<__bf16*>(out);
+  a.nq = d.nq;
+  a.kv_len = kv_len;
+  a.hc = d.head_count;
+  a.c = h.c;
+  a.rope = h.geom;
+  if (vdit::launch_attn_fwd(a, d.head_dim, d.use_rope != 0, s) != hipSuccess) return VDIT_ERR_DEVICE;
+  return VDIT_OK;
+}
+
+vdit_status_t check_out(const vdit_attn& h, const Inputs& in, void* out, const void* ws) {
+  if (!out) return VDIT_ERR_INVALID_ARG;
+  if (!aligned16(out)) return VDIT_ERR_ALIGNMENT;
+  const size_t ob = (size_t)h.desc.nq * h.desc.head_count * h.desc.head_dim * 2;
+  if (overlaps(out, ob, in.q_base, in.q_bytes) || overlaps(out, ob, in.k_base, in.k_bytes) ||
+      overlaps(out, ob, in.v_base, in.v_bytes) || overlaps(out, ob, ws, h.ws_total))
+    return VDIT_ERR_INVALID_ARG;
+  return VDIT_OK;
+}
+
+vdit_status_t check_ws_inputs(const vdit_attn& h, const Inputs& in, const void* ws) {
+  if (overlaps(ws, h.ws_total, in.q_base, in.q_bytes) || overlaps(ws, h.ws_total, in.k_base, in.k_bytes) ||
+      overlaps(ws, h.ws_total, in.v_base, in.v_bytes))
+    return VDIT_ERR_INVALID_ARG;
+  return VDIT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+vdit_status_t vdit_attn_ulysses_heads(int32_t heads_total, int32_t degree, int32_t rank, int32_t* head_begin,
+                                      int32_t* head_count) {
+  if (!head_begin || !head_count) return VDIT_ERR_INVALID_ARG;
+  if (heads_total <= 0 || degree <= 0 || heads_total % degree != 0) return VDIT_ERR_INVALID_ARG;
+  if (rank < 0 || rank >= degree) return VDIT_ERR_INVALID_ARG;
+  const int32_t per = heads_total / degree;
+  *head_begin = rank * per;
+  *head_count = per;
+  return VDIT_OK;
+}
+
+vdit_status_t vdit_attn_create(const vdit_attn_desc_t* desc, vdit_attn_t* out) {
+  if (!desc || !out) return VDIT_ERR_INVALID_ARG;
+  *out = nullptr;
+  const vdit_status_t st = validate_desc(*desc);
+  if (st != VDIT_OK) return st;
+
+  vdit_attn* hp = new (std::nothrow) vdit_attn{};
+  if (!hp) return VDIT_ERR_OUT_OF_MEMORY;
+  vdit_attn& h = *hp;
+  h.desc = *desc;
+  const vdit_attn_desc_t& d = h.desc;
+  const double scale = d.scale > 0.0f ? (double)d.scale : 1.0 / std::sqrt((double)d.head_dim);
+  h.scale = (float)scale;
+  h.c = (float)(scale * 1.4426950408889634);  // log2(e)
+  h.nk_pad = ((int64_t)d.nk + vdit::kBlockN - 1) / vdit::kBlockN * vdit::kBlockN;
+  const size_t per_head = (size_t)h.nk_pad * d.head_dim * 2;
+  h.ws_vt_off = 0;
+  h.ws_vt_bytes = per_head * d.head_count;
+  h.ws_kr_off = align_up(h.ws_vt_bytes, 256);
+  h.ws_kr_bytes = d.use_rope ? per_head * d.head_count : 0;
+  h.ws_total = d.use_rope ? h.ws_kr_off + h.ws_kr_bytes : h.ws_vt_bytes;
+  h.rope_tab = nullptr;
+  h.geom = vdit::RopeGeom{};
+
+  if (hipGetDevice(&h.device) != hipSuccess) {
+    delete hp;
+    return VDIT_ERR_DEVICE;
+  }
+  if (d.use_rope) {
+    std::vector<float2> tab;
+    build_rope_table(d, tab, h.geom);
+    if (hipMalloc(reinterpret_cast<void**>(&h.rope_tab), tab.size() * sizeof(float2)) != hipSuccess) {
+      (void)hipGetLastError();
+      delete hp;
+      return VDIT_ERR_OUT_OF_MEMORY;
+    }
+    if (hipMemcpy(h.rope_tab, tab.data(), tab.size() * sizeof(float2), hipMemcpyHostToDevice) != hipSuccess) {
+      (void)hipFree(h.rope_tab);
+      delete hp;
+      return VDIT_ERR_DEVICE;
+    }
+    h.geom.tab = h.rope_tab;
+  }
+  {
+    std::lock_guard<std::mutex> lk(g_live_mu);
+    live_handles().insert(hp);
+  }
+  *out = hp;
+  return VDIT_OK;
+}
+
+vdit_status_t vdit_attn_destroy(vdit_attn_t h) {
+  if (!h) return VDIT_OK;
+  {
+    std::lock_guard<std::mutex> lk(g_live_mu);
+    if (live_handles().erase(h) == 0) return VDIT_ERR_INVALID_ARG;
+  }
+  vdit_status_t st = VDIT_OK;
+  if (h->rope_tab && hipFree(h->rope_tab) != hipSuccess) st = VDIT_ERR_DEVICE;
+  delete h;
+  return st;
+}
+
+vdit_status_t vdit_attn_workspace_bytes(vdit_attn_t h, size_t* bytes) {
+  if (!is_live(h) || !bytes) return VDIT_ERR_INVALID_ARG;
+  *bytes = h->ws_total;
+  return VDIT_OK;
+}
+
+vdit_status_t vdit_attn_prepare(vdit_attn_t h, const void* q, const void* k, const void* v, int32_t key_len,
+                                void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (!is_live(h)) return VDIT_ERR_INVALID_ARG;
+  Inputs in{};
+  vdit_status_t st = resolve_inputs(*h, q, k, v, in);
+  if (st != VDIT_OK) return st;
+  int32_t kv_len = 0;
+  if ((st = check_call(*h, key_len, workspace, workspace_bytes, kv_len)) != VDIT_OK) return st;
+  if ((st = check_ws_inputs(*h, in, workspace)) != VDIT_OK) return st;
+  return do_prepare(*h, in, kv_len, workspace, static_cast<hipStream_t>(hip_stream));
+}
+
+vdit_status_t vdit_attn_attend(vdit_attn_t h, const void* q, const void* k, const void* v, int32_t key_len,
+                               void* out, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (!is_live(h)) return VDIT_ERR_INVALID_ARG;
+  Inputs in{};
+  vdit_status_t st = resolve_inputs(*h, q, k, v, in);
+  if (st != VDIT_OK) return st;
+  if ((st = check_out(*h, in, out, workspace)) != VDIT_OK) return st;
+  int32_t kv_len = 0;
+  if ((st = check_call(*h, key_len, workspace, workspace_bytes, kv_len)) != VDIT_OK) return st;
+  if ((st = check_ws_inputs(*h, in, workspace)) != VDIT_OK) return st;
+  return do_attend(*h, in, kv_len, out, workspace, static_cast<hipStream_t>(hip_stream));
+}
+
+vdit_status_t vdit_attn_fwd(vdit_attn_t h, const void* q, const void* k, const void* v, int32_t key_len, void* out,
+                            void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (!is_live(h)) return VDIT_ERR_INVALID_ARG;
+  Inputs in{};
+  vdit_status_t st = resolve_inputs(*h, q, k, v, in);
+  if (st != VDIT_OK) return st;
+  if ((st = check_out(*h, in, out, workspace)) != VDIT_OK) return st;
+  int32_t kv_len = 0;
+  if ((st = check_call(*h, key_len, workspace, workspace_bytes, kv_len)) != VDIT_OK) return st;
+  if ((st = check_ws_inputs(*h, in, workspace)) != VDIT_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  if ((st = do_prepare(*h, in, kv_len, workspace, s)) != VDIT_OK) return st;
+  return do_attend(*h, in, kv_len, out, workspace, s);
+}
+
+static vdit_status_t pack_common(const void* src, void* dst, int32_t n, int32_t ht, int32_t d, int32_t groups,
+                                 bool unpack, void* hip_stream) {
+  if (!src || !dst || n <= 0 || ht <= 0 || d <= 0 || groups <= 0 || ht % groups != 0) return VDIT_ERR_INVALID_ARG;
+  if (!aligned16(src) || !aligned16(dst) || (d * 2) % 16 != 0) return VDIT_ERR_ALIGNMENT;
+  const size_t bytes = (size_t)n * ht * d * 2;
+  if (overlaps(src, bytes, dst, bytes)) return VDIT_ERR_INVALID_ARG;
+  if ((int64_t)ht * (d / 8) > (int64_t(1) << 30)) return VDIT_ERR_UNSUPPORTED;
+  if (vdit::launch_pack(src, dst, n, ht, d, groups, unpack, static_cast<hipStream_t>(hip_stream)) != hipSuccess)
+    return VDIT_ERR_DEVICE;
+  return VDIT_OK;
+}
+
+vdit_status_t vdit_pack_heads(const void* src, void* dst, int32_t n, int32_t heads_total, int32_t head_dim,
+                              int32_t groups, void* hip_stream) {
+  return pack_common(src, dst, n, heads_total, head_dim, groups, false, hip_stream);
+}
+
+vdit_status_t vdit_unpack_heads(const void* src, void* dst, int32_t n, int32_t heads_total, int32_t head_dim,
+                                int32_t groups, void* hip_stream) {
+  return pack_common(src, dst, n, heads_total, head_dim, groups, true, hip_stream);
+}
+
+vdit_status_t vdit_attn_rope_probe(vdit_attn_t h, int32_t* idx_out, void* hip_stream) {
+  if (!is_live(h) || !idx_out) return VDIT_ERR_INVALID_ARG;
+  if (!h->desc.use_rope) return VDIT_ERR_INVALID_ARG;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != h->device) return VDIT_ERR_DEVICE;
+  if (vdit::launch_rope_probe(h->geom, h->desc.nq, h->desc.head_dim, idx_out, static_cast<hipStream_t>(hip_stream)) !=
+      hipSuccess)
+    return VDIT_ERR_DEVICE;
+  return VDIT_OK;
+}
+
+const char* vdit_status_string(vdit_status_t s) {
+  switch (s) {
+    case VDIT_OK: return "VDIT_OK";
+    case VDIT_ERR_INVALID_ARG: return "VDIT_ERR_INVALID_ARG: invalid argument or shape";
+    case VDIT_ERR_UNSUPPORTED: return "VDIT_ERR_UNSUPPORTED: valid request outside what the kernels implement";
+    case VDIT_ERR_ALIGNMENT: return "VDIT_ERR_ALIGNMENT: device pointer not 16-byte aligned";
+    case VDIT_ERR_OUT_OF_MEMORY: return "VDIT_ERR_OUT_OF_MEMORY: device table allocation failed";
+    case VDIT_ERR_DEVICE: return "VDIT_ERR_DEVICE: HIP call or kernel launch failed, or wrong device current";
+    case VDIT_ERR_WORKSPACE: return "VDIT_ERR_WORKSPACE: workspace missing or too small";
+  }
+  return "VDIT_ERR_UNKNOWN: unknown status code";
+}
+
+}  // extern "C"

@@ -1,0 +1,127 @@
+// Internal definitions shared by the gfx950 kernels and the C-ABI host code.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vdit {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kBlockN = 64;  // keys per K/V tile
+
+// 3D RoPE geometry shared by the q prologue, the k pre-pass and the index probe.
+// Pair p of the head dimension belongs to band 0 (t) for p < pair_h, band 1 (y)
+// for pair_h <= p < pair_w, band 2 (x) otherwise; i is its index inside the band.
+// cos/sin of band b at position pos and index i sit at tab[off_b + pos * half_b + i].
+struct RopeGeom {
+  const float2* tab;  // device table (cos, sin)
+  int32_t grid_h, grid_w;
+  int32_t pair_h, pair_w;          // first pair of the h and w bands
+  int32_t half_t, half_h, half_w;  // pairs per band
+  int32_t off_h, off_w;            // table offsets of the h and w bands (t band at 0)
+};
+
+struct RopeIndex {
+  int32_t band, i, pos;
+};
+
+__device__ __forceinline__ void rope_token_pos(const RopeGeom& g, int32_t n, int32_t& t, int32_t& y, int32_t& x) {
+  const int32_t hw = g.grid_h * g.grid_w;
+  t = n / hw;
+  const int32_t r = n - t * hw;
+  y = r / g.grid_w;
+  x = r - y * g.grid_w;
+}
+
+__device__ __forceinline__ RopeIndex rope_pair_index(const RopeGeom& g, int32_t p, int32_t t, int32_t y, int32_t x) {
+  RopeIndex r;
+  if (p < g.pair_h) {
+    r.band = 0; r.i = p; r.pos = t;
+  } else if (p < g.pair_w) {
+    r.band = 1; r.i = p - g.pair_h; r.pos = y;
+  } else {
+    r.band = 2; r.i = p - g.pair_w; r.pos = x;
+  }
+  return r;
+}
+
+__device__ __forceinline__ float2 rope_cos_sin(const RopeGeom& g, const RopeIndex& r) {
+  int32_t idx;
+  if (r.band == 0) idx = r.pos * g.half_t + r.i;
+  else if (r.band == 1) idx = g.off_h + r.pos * g.half_h + r.i;
+  else idx = g.off_w + r.pos * g.half_w + r.i;
+  return g.tab[idx];
+}
+
+__device__ __forceinline__ float bf16_to_f32(__bf16 v) { return (float)v; }
+
+// Rotate the 8 consecutive elements [d0, d0 + 8) of one token row (4 pairs) and
+// round back to bfloat16. Fixed arithmetic: a' = fma(a, c, -(b*s)), b' = fma(a, s, b*c).
+__device__ __forceinline__ bf16x8 rope_chunk(const RopeGeom& g, bf16x8 v, int32_t d0, int32_t t, int32_t y, int32_t x) {
+  bf16x8 o;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const RopeIndex ri = rope_pair_index(g, (d0 >> 1) + m, t, y, x);
+    const float2 cs = rope_cos_sin(g, ri);
+    const float a = (float)v[2 * m];
+    const float b = (float)v[2 * m + 1];
+    const float ra = __builtin_fmaf(a, cs.x, -(b * cs.y));
+    const float rb = __builtin_fmaf(a, cs.y, b * cs.x);
+    o[2 * m] = (__bf16)ra;
+    o[2 * m + 1] = (__bf16)rb;
+  }
+  return o;
+}
+
+// ---------------------------------------------------------------------------
+// Launch parameter blocks.
+// ---------------------------------------------------------------------------
+
+struct AttnArgs {
+  const __bf16* q;       // q of head `head_begin`, token 0
+  int64_t q_row;         // elements between consecutive tokens of q
+  const __bf16* k;       // k of local head 0, key 0 (input or rotated workspace copy)
+  int64_t k_row;         // elements between consecutive keys
+  int64_t k_head;        // elements between consecutive local heads of k
+  const _Float16* vt;    // transposed float16 v in the workspace, local head 0
+  int64_t vt_head;       // elements between heads of vt
+  __bf16* out;           // [nq, hc, d]
+  int32_t nq;
+  int32_t kv_len;        // valid keys
+  int32_t hc;            // heads in the share
+  int32_t n_qtiles;      // query tiles per head
+  float c;               // scale * log2(e)
+  int32_t q_head;        // elements between consecutive heads of q (= d)
+  RopeGeom rope;
+};
+
+struct PrepArgs {
+  const __bf16* k;       // k of head `head_begin`, key 0
+  const __bf16* v;       // v of head `head_begin`, key 0
+  int64_t kv_row;        // elements between consecutive keys
+  int64_t kv_head;       // elements between consecutive heads (= d)
+  _Float16* vt;          // workspace vt, local head 0
+  int64_t vt_head;
+  __bf16* kr;            // workspace rotated k, local head 0 (nullptr without RoPE)
+  int64_t kr_head;
+  int32_t kv_len;
+  int32_t n_ktiles;      // ceil(kv_len / 64)
+  int32_t hc;
+  RopeGeom rope;
+};
+
+// Host-side launchers (defined in the kernel translation units).
+hipError_t launch_attn_fwd(const AttnArgs& a, int head_dim, bool rope_q, hipStream_t s);
+hipError_t launch_prepare(const PrepArgs& a, int head_dim, bool rope_k, hipStream_t s);
+hipError_t launch_pack(const void* src, void* dst, int64_t n, int32_t ht, int32_t d, int32_t groups,
+                       bool unpack, hipStream_t s);
+hipError_t launch_rope_probe(const RopeGeom& g, int32_t nq, int32_t head_dim, int32_t* out, hipStream_t s);
+
+}  // namespace vdit

@@ -1,0 +1,138 @@
+// Bandwidth-bound kernels around the attention kernel:
+//   * prepare: v of the head share -> float16 V^T tiles in the workspace (keys
+//     permuted inside groups of 16 to match the weight layout of the attention
+//     kernel, zero past the valid keys), and with RoPE the rotated keys;
+//   * pack / unpack: [n, Ht, d] <-> [G, n, Ht/G, d] for the Ulysses exchange;
+//   * rope probe: the (t, y, x, band, i) index map as the kernels compute it.
+#include "common.hpp"
+
+namespace vdit {
+namespace {
+
+// Position of key k (0..63) inside a prepared 64-key V^T tile: bits 2 and 3 of
+// the index are swapped. In the 32x32 accumulator of S^T a lane of half h holds,
+// for 16 consecutive keys, keys {4h..4h+3} then {8+4h..8+4h+3}; after the swap
+// those eight keys are adjacent, so one 16-byte read gives the lane its operand.
+__device__ __forceinline__ int vt_position(int k) {
+  return (k & ~15) | (k & 3) | ((k >> 1) & 4) | ((k << 1) & 8);
+}
+
+template <int D, bool ROPE>
+__global__ void __launch_bounds__(256) prepare_kernel(PrepArgs a) {
+  constexpr int kChunks = D / 8;
+  constexpr int kLoads = kBlockN * kChunks / 256;
+  constexpr int kPad = kBlockN + 8;  // float16 per LDS row: 144 bytes, keeps 16-byte alignment
+  __shared__ __attribute__((aligned(16))) _Float16 tr[D * kPad];
+
+  const int tile = blockIdx.x;
+  const int head = blockIdx.y;
+  const int tid = threadIdx.x;
+  const __bf16* vsrc = a.v + (int64_t)head * a.kv_head;
+
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const int qd = i * 256 + tid;
+    const int kl = qd / kChunks;
+    const int ch = qd % kChunks;
+    const int key = tile * kBlockN + kl;
+    bf16x8 v = bf16x8{};
+    if (key < a.kv_len) v = *reinterpret_cast<const bf16x8*>(vsrc + (int64_t)key * a.kv_row + ch * 8);
+    const int pos = vt_position(kl);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tr[(ch * 8 + e) * kPad + pos] = (_Float16)(float)v[e];
+  }
+  __syncthreads();
+  _Float16* dst = a.vt + (int64_t)head * a.vt_head + (int64_t)tile * (D * kBlockN);
+#pragma unroll
+  for (int i = 0; i < D * (kBlockN / 8) / 256; ++i) {
+    const int qd = i * 256 + tid;
+    const int row = qd >> 3;
+    const int ch = qd & 7;
+    *reinterpret_cast<u32x4*>(dst + row * kBlockN + ch * 8) =
+        *reinterpret_cast<const u32x4*>(&tr[row * kPad + ch * 8]);
+  }
+
+  if constexpr (ROPE) {
+    const __bf16* ksrc = a.k + (int64_t)head * a.kv_head;
+    __bf16* kdst = a.kr + (int64_t)head * a.kr_head;
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int qd = i * 256 + tid;
+      const int kl = qd / kChunks;
+      const int ch = qd % kChunks;
+      const int key = tile * kBlockN + kl;
+      bf16x8 v = bf16x8{};
+      if (key < a.kv_len) {
+        v = *reinterpret_cast<const bf16x8*>(ksrc + (int64_t)key * a.kv_row + ch * 8);
+        int t, y, x;
+        rope_token_pos(a.rope, key, t, y, x);
+        v = rope_chunk(a.rope, v, ch * 8, t, y, x);
+      }
+      *reinterpret_cast<bf16x8*>(kdst + (int64_t)key * D + ch * 8) = v;
+    }
+  }
+}
+
+// One workgroup per token row: moves that token's Ht * d elements between the
+// [n, Ht, d] and [G, n, Ht/G, d] layouts in 16-byte chunks.
+__global__ void __launch_bounds__(256) pack_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                   int64_t n, int32_t ht, int32_t cpr, int32_t hg, int32_t unpack) {
+  const int64_t t = blockIdx.x;
+  const int32_t row_chunks = ht * cpr;   // chunks of one token
+  const int32_t grp_chunks = hg * cpr;   // chunks of one token inside one group
+  for (int32_t i = threadIdx.x; i < row_chunks; i += 256) {
+    const int32_t g = i / grp_chunks;
+    const int32_t r = i - g * grp_chunks;
+    const int64_t flat = t * row_chunks + i;                  // [n, Ht, d] index
+    const int64_t grouped = (g * n + t) * grp_chunks + r;     // [G, n, Ht/G, d] index
+    if (unpack) dst[flat] = src[grouped];
+    else dst[grouped] = src[flat];
+  }
+}
+
+__global__ void __launch_bounds__(256) rope_probe_kernel(RopeGeom g, int32_t nq, int32_t pairs, int32_t* out) {
+  const int64_t total = (int64_t)nq * pairs;
+  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
+    const int32_t n = (int32_t)(idx / pairs);
+    const int32_t p = (int32_t)(idx - (int64_t)n * pairs);
+    int t, y, x;
+    rope_token_pos(g, n, t, y, x);
+    const RopeIndex r = rope_pair_index(g, p, t, y, x);
+    int32_t* o = out + idx * 5;
+    o[0] = t; o[1] = y; o[2] = x; o[3] = r.band; o[4] = r.i;
+  }
+}
+
+template <int D, bool ROPE>
+hipError_t launch_prepare_t(const PrepArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((prepare_kernel<D, ROPE>), dim3(a.n_ktiles, a.hc), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prepare(const PrepArgs& a, int head_dim, bool rope_k, hipStream_t s) {
+  if (a.n_ktiles <= 0 || a.hc <= 0 || a.hc > 65535) return hipErrorInvalidValue;
+  if (head_dim == 128) return rope_k ? launch_prepare_t<128, true>(a, s) : launch_prepare_t<128, false>(a, s);
+  if (head_dim == 64) return rope_k ? launch_prepare_t<64, true>(a, s) : launch_prepare_t<64, false>(a, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_pack(const void* src, void* dst, int64_t n, int32_t ht, int32_t d, int32_t groups,
+                       bool unpack, hipStream_t s) {
+  if (n <= 0 || n > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)n), dim3(256), 0, s, reinterpret_cast<const u32x4*>(src),
+                     reinterpret_cast<u32x4*>(dst), n, ht, d / 8, ht / groups, unpack ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_probe(const RopeGeom& g, int32_t nq, int32_t head_dim, int32_t* out, hipStream_t s) {
+  const int64_t total = (int64_t)nq * (head_dim / 2);
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(rope_probe_kernel, dim3((unsigned)blocks), dim3(256), 0, s, g, nq, head_dim / 2, out);
+  return hipGetLastError();
+}
+
+}  // namespace vdit

@@ -1,0 +1,354 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Tolerances on the bfloat16 outputs: max |gpu - ref| <= 2e-2 and
+sum |gpu - ref| / sum |ref| <= 2e-3, with ref the unrounded float64 oracle.
+Large workloads are checked on sampled query rows (every selected head and
+every element of each row) plus the rows at tile edges and the ragged end.
+Layout, head selection, packing and the RoPE index map are checked bit for bit.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic_inputs as si
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 2e-2
+REL_L1 = 2e-3
+ROPE5 = {"grid": (32, 64, 64), "dims": (44, 42, 42), "base": 10000.0}
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU in this environment")
+    import long_sequence_attention_amd as vd
+    vd.load_library()  # raises if the HIP library is missing on a GPU machine
+    return torch.device("cuda:0")
+
+
+def vdm():
+    import long_sequence_attention_amd as vd
+    return vd
+
+
+def up(bits, dev):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def down(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def as_f64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def note(msg):
+    print(f"[gpu] {msg}", flush=True)
+
+
+def check(got, ref, label):
+    err = np.abs(got - ref)
+    mx = float(err.max())
+    rel = float(err.sum() / np.abs(ref).sum())
+    note(f"{label}: max|d|={mx:.3e} relL1={rel:.3e} ({ref.size} elements)")
+    assert np.all(np.isfinite(got)), label
+    assert mx <= MAX_ABS, f"{label}: max|d| {mx}"
+    assert rel <= REL_L1, f"{label}: relL1 {rel}"
+    return mx, rel
+
+
+def nhd_inputs(n, nk, ht, d, seed, sigma=1.0):
+    return (si.normal_bf16((n, ht, d), seed, si.STREAM_Q, sigma),
+            si.normal_bf16((nk, ht, d), seed, si.STREAM_K, sigma),
+            si.normal_bf16((nk, ht, d), seed, si.STREAM_V, sigma))
+
+
+def run_nhd(dev, q, k, v, *, head_begin=0, head_count=None, key_len=None, scale=0.0):
+    vd = vdm()
+    nq, ht, d = q.shape
+    nk = k.shape[0]
+    attn = vd.Attention(nq, nk, ht, d, head_begin=head_begin, head_count=head_count,
+                        use_key_mask=key_len is not None, scale=scale)
+    out = attn.forward(up(q, dev), up(k, dev), up(v, dev), key_len=key_len or 0)
+    torch.cuda.synchronize()
+    return out
+
+
+# ---------------------------------------------------------------------------
+# The five workloads
+# ---------------------------------------------------------------------------
+
+def test_cfg1_small_d64_all_rows(dev):
+    note("cfg1 N=256 H=2 d=64 seed 1001")
+    q, k, v = nhd_inputs(256, 256, 2, 64, 1001)
+    out = run_nhd(dev, q, k, v)
+    check(as_f64(out), oracle.mha_reference(q, k, v), "cfg1")
+
+
+def test_cfg2_n4096_h10_all_rows(dev):
+    note("cfg2 N=4096 H=10 d=128 seed 1002")
+    q, k, v = nhd_inputs(4096, 4096, 10, 128, 1002)
+    out = run_nhd(dev, q, k, v)
+    check(as_f64(out), oracle.mha_reference(q, k, v), "cfg2")
+
+
+@pytest.mark.timeout(900)
+def test_cfg3_ulysses_share_n75600(dev):
+    n = 21 * 45 * 80
+    note(f"cfg3 N={n} Ht=40 heads 0-9 d=128 seed 1003")
+    q, k, v = nhd_inputs(n, n, 40, 128, 1003)
+    out = run_nhd(dev, q, k, v, head_begin=0, head_count=10)
+    rows = si.sample_rows(n, 4096, 1003, si.tile_edge_rows(n))
+    got = as_f64(out[torch.from_numpy(rows).to(dev)])
+    ref = oracle.mha_reference(q, k, v, head_begin=0, head_count=10, rows=rows)
+    check(got, ref, f"cfg3 ({len(rows)} rows x 10 heads)")
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("fixed_len", [None, 64, 512])
+def test_cfg4_cross_attention_key_mask(dev, fixed_len):
+    nq, nk = 75600, 512
+    L = si.key_length(1004) if fixed_len is None else fixed_len
+    note(f"cfg4 Nq={nq} Nk={nk} L={L} H=40 d=128 seed 1004")
+    q, k, v = nhd_inputs(nq, nk, 40, 128, 1004)
+    out = run_nhd(dev, q, k, v, key_len=L)
+    rows = si.sample_rows(nq, 4096, 1004, si.tile_edge_rows(nq))
+    got = as_f64(out[torch.from_numpy(rows).to(dev)])
+    ref = oracle.mha_reference(q, k, v, rows=rows, key_len=L)
+    check(got, ref, f"cfg4 L={L}")
+
+
+@pytest.mark.timeout(1200)
+def test_cfg5_packed_rope_n131072(dev):
+    vd = vdm()
+    n = 32 * 64 * 64
+    note(f"cfg5 packed N={n} H=40 d=128 RoPE 44/42/42 sigma=0.5 seed 1005")
+    qkv = si.normal_bf16((n, 3, 40, 128), 1005, si.STREAM_Q, 0.5)
+    attn = vd.Attention(n, n, 40, 128, layout="N3HD", rope=ROPE5)
+    out = attn.forward(up(qkv, dev))
+    torch.cuda.synchronize()
+    rows = si.sample_rows(n, 1024, 1005, si.tile_edge_rows(n))
+    got = as_f64(out[torch.from_numpy(rows).to(dev)])
+    del out
+    ref = oracle.mha_reference(qkv, layout="N3HD", rows=rows, rope=ROPE5)
+    check(got, ref, f"cfg5 ({len(rows)} rows x 40 heads)")
+
+
+# ---------------------------------------------------------------------------
+# Ragged sizes, head offsets, key lengths, head dims
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n", [1, 15, 16, 17, 63, 65, 127, 129, 255, 257, 1000, 4097])
+@pytest.mark.parametrize("d", [64, 128])
+def test_ragged_lengths(dev, n, d):
+    note(f"ragged N={n} d={d}")
+    q, k, v = nhd_inputs(n, n, 3, d, 2000 + n)
+    out = run_nhd(dev, q, k, v, head_begin=1, head_count=2)
+    check(as_f64(out), oracle.mha_reference(q, k, v, head_begin=1, head_count=2), f"ragged N={n} d={d}")
+
+
+@pytest.mark.parametrize("h0", [0, 10, 30])
+def test_head_offsets(dev, h0):
+    note(f"head offset {h0}")
+    q, k, v = nhd_inputs(700, 700, 40, 128, 3000 + h0)
+    out = run_nhd(dev, q, k, v, head_begin=h0, head_count=10)
+    check(as_f64(out), oracle.mha_reference(q, k, v, head_begin=h0, head_count=10), f"h0={h0}")
+
+
+@pytest.mark.parametrize("L", [1, 2, 63, 64, 65, 511, 512])
+def test_key_lengths(dev, L):
+    note(f"key length {L}")
+    q, k, v = nhd_inputs(600, 512, 4, 128, 4000 + L)
+    out = run_nhd(dev, q, k, v, key_len=L)
+    check(as_f64(out), oracle.mha_reference(q, k, v, key_len=L), f"L={L}")
+
+
+def test_cross_attention_more_keys_than_queries(dev):
+    q, k, v = nhd_inputs(50, 3000, 2, 128, 4500)
+    out = run_nhd(dev, q, k, v)
+    check(as_f64(out), oracle.mha_reference(q, k, v), "nq < nk")
+
+
+def test_explicit_scale(dev):
+    q, k, v = nhd_inputs(300, 300, 2, 64, 4600)
+    out = run_nhd(dev, q, k, v, scale=0.05)
+    check(as_f64(out), oracle.mha_reference(q, k, v, scale=0.05), "scale 0.05")
+
+
+@pytest.mark.parametrize("grid,dims,d", [((3, 5, 7), (44, 42, 42), 128), ((4, 4, 16), (24, 20, 20), 64),
+                                         ((1, 1, 300), (44, 42, 42), 128)])
+def test_rope_small_grids(dev, grid, dims, d):
+    vd = vdm()
+    n = grid[0] * grid[1] * grid[2]
+    rope = {"grid": grid, "dims": dims, "base": 10000.0}
+    note(f"rope grid={grid} d={d}")
+    qkv = si.normal_bf16((n, 3, 2, d), 5000 + n, 0, 0.5)
+    out = vd.Attention(n, n, 2, d, layout="N3HD", rope=rope).forward(up(qkv, dev))
+    torch.cuda.synchronize()
+    check(as_f64(out), oracle.mha_reference(qkv, layout="N3HD", rope=rope), f"rope {grid}")
+
+
+def test_rope_nhd_layout_with_head_share(dev):
+    vd = vdm()
+    grid = (2, 8, 16)
+    n = 256
+    rope = {"grid": grid, "dims": (44, 42, 42), "base": 10000.0}
+    q, k, v = nhd_inputs(n, n, 8, 128, 5100, 0.5)
+    out = vd.Attention(n, n, 8, 128, head_begin=4, head_count=4, rope=rope).forward(up(q, dev), up(k, dev), up(v, dev))
+    torch.cuda.synchronize()
+    check(as_f64(out), oracle.mha_reference(q, k, v, head_begin=4, head_count=4, rope=rope), "rope NHD share")
+
+
+# ---------------------------------------------------------------------------
+# Bitwise identities
+# ---------------------------------------------------------------------------
+
+def test_head_share_equals_slice_of_all_heads(dev):
+    # a Ulysses head share computes bit for bit the same values as inside an all-heads call
+    vd = vdm()
+    q, k, v = nhd_inputs(2000, 2000, 40, 128, 6000)
+    full = run_nhd(dev, q, k, v)
+    for r in range(4):
+        b, c = vd.ulysses_heads(40, 4, r)
+        part = run_nhd(dev, q, k, v, head_begin=b, head_count=c)
+        assert torch.equal(part.view(torch.int16), full[:, b:b + c].contiguous().view(torch.int16)), r
+
+
+def test_packed_equals_separate(dev):
+    vd = vdm()
+    n = 1500
+    qkv = si.normal_bf16((n, 3, 6, 128), 6100, 0)
+    a = vd.Attention(n, n, 6, 128, layout="N3HD", head_begin=2, head_count=3).forward(up(qkv, dev))
+    b = run_nhd(dev, qkv[:, 0].copy(), qkv[:, 1].copy(), qkv[:, 2].copy(), head_begin=2, head_count=3)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_masked_keys_have_no_effect_and_nan_does_not_leak(dev):
+    q, k, v = nhd_inputs(400, 512, 4, 128, 6200)
+    L = 300
+    base = run_nhd(dev, q, k, v, key_len=L)
+    k2, v2 = k.copy(), v.copy()
+    k2[L:] = si.normal_bf16(k2[L:].shape, 99, 5, 100.0)
+    v2[L:] = 0x7FC0  # NaN
+    k2[L + 7:] = 0x7F80  # +inf
+    other = run_nhd(dev, q, k2, v2, key_len=L)
+    assert torch.equal(base.view(torch.int16), other.view(torch.int16))
+    assert bool(torch.isfinite(other.float()).all())
+
+
+def test_deterministic_run_to_run(dev):
+    vd = vdm()
+    q, k, v = nhd_inputs(3000, 3000, 4, 128, 6300)
+    attn = vd.Attention(3000, 3000, 4, 128)
+    qd, kd, vd_ = up(q, dev), up(k, dev), up(v, dev)
+    a = attn.forward(qd, kd, vd_)
+    b = attn.forward(qd, kd, vd_)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_output_guard_bands_untouched(dev):
+    vd = vdm()
+    n, ht, d = 333, 4, 128
+    q, k, v = nhd_inputs(n, n, ht, d, 6400)
+    attn = vd.Attention(n, n, ht, d, head_begin=1, head_count=2)
+    guard = 4096
+    size = n * 2 * d
+    buf = torch.full((size + 2 * guard,), 12345, dtype=torch.int16, device=dev)
+    out = buf[guard:guard + size].view(torch.bfloat16).view(n, 2, d)
+    ws_guard = 8192
+    wsbuf = torch.full((attn.workspace_bytes + 2 * ws_guard,), 0x5A, dtype=torch.uint8, device=dev)
+    ws = wsbuf[ws_guard:ws_guard + attn.workspace_bytes]
+    attn.forward(up(q, dev), up(k, dev), up(v, dev), out=out, workspace=ws)
+    torch.cuda.synchronize()
+    assert bool((buf[:guard] == 12345).all()) and bool((buf[guard + size:] == 12345).all())
+    assert bool((wsbuf[:ws_guard] == 0x5A).all()) and bool((wsbuf[-ws_guard:] == 0x5A).all())
+    check(as_f64(out), oracle.mha_reference(q, k, v, head_begin=1, head_count=2), "guarded out")
+
+
+def test_rope_probe_matches_oracle_index_map(dev):
+    vd = vdm()
+    grid = (21, 45, 80)
+    n = 21 * 45 * 80
+    attn = vd.Attention(n, n, 40, 128, rope={"grid": grid, "dims": (44, 42, 42), "base": 10000.0})
+    got = attn.rope_probe(dev).cpu().numpy()
+    torch.cuda.synchronize()
+    want = oracle.rope_index_table(np.arange(n), grid, 128, (44, 42, 42))
+    assert np.array_equal(got, want)
+
+
+def test_pack_unpack_roundtrip_and_permute(dev):
+    vd = vdm()
+    for n, ht, d, g in [(1000, 40, 128, 4), (18900, 40, 128, 4), (333, 12, 64, 3), (77, 40, 128, 8)]:
+        x = up(si.normal_bf16((n, ht, d), 7000 + n, 0), dev)
+        p = vd.pack_heads(x, g)
+        ref = x.view(n, g, ht // g, d).permute(1, 0, 2, 3).contiguous()
+        assert torch.equal(p.view(torch.int16), ref.view(torch.int16))
+        back = vd.unpack_heads(p)
+        assert torch.equal(back.view(torch.int16), x.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# Closed forms and invariants on the GPU
+# ---------------------------------------------------------------------------
+
+def test_single_valid_key_returns_its_value_row(dev):
+    q, k, v = nhd_inputs(300, 64, 3, 128, 8000)
+    out = run_nhd(dev, q, k, v, key_len=1)
+    want = np.broadcast_to(v[0][None], (300, 3, 128))
+    assert np.array_equal(down(out), want)
+
+
+def test_constant_values_give_constant_output(dev):
+    q, k, v = nhd_inputs(500, 500, 2, 128, 8100)
+    v[:] = v[0:1]
+    out = run_nhd(dev, q, k, v)
+    want = np.broadcast_to(v[0][None], (500, 2, 128))
+    # the weights sum to the normaliser up to float32 rounding: within one bf16 ulp
+    got = as_f64(out)
+    w = si.bf16_bits_to_f32(want).astype(np.float64)
+    assert np.all(np.abs(got - w) <= np.abs(w) * 2.0 ** -7 + 1e-30)
+
+
+def test_zero_queries_average_the_values(dev):
+    q, k, v = nhd_inputs(200, 700, 2, 128, 8200)
+    q[:] = 0
+    out = run_nhd(dev, q, k, v)
+    ref = oracle.mha_reference(q, k, v)
+    check(as_f64(out), ref, "q=0 mean of values")
+
+
+# ---------------------------------------------------------------------------
+# Errors reported through the ABI on a live device
+# ---------------------------------------------------------------------------
+
+def test_call_errors(dev):
+    vd = vdm()
+    q, k, v = nhd_inputs(256, 256, 2, 64, 9000)
+    qd, kd, vd_ = up(q, dev), up(k, dev), up(v, dev)
+    attn = vd.Attention(256, 256, 2, 64, use_key_mask=True)
+    for bad in (0, 257, -3):
+        with pytest.raises(vd.VditError) as e:
+            attn.forward(qd, kd, vd_, key_len=bad)
+        assert e.value.code == 1
+    small = torch.empty(max(attn.workspace_bytes - 256, 16), dtype=torch.uint8, device=dev)
+    with pytest.raises(vd.VditError) as e:
+        attn.forward(qd, kd, vd_, key_len=10, workspace=small)
+    assert e.value.code == 6
+    raw = torch.empty(256 * 2 * 64 + 8, dtype=torch.bfloat16, device=dev)
+    mis = raw[1:1 + 256 * 2 * 64].view(256, 2, 64)
+    with pytest.raises(vd.VditError) as e:
+        attn.forward(qd, kd, vd_, key_len=10, out=mis)
+    assert e.value.code == 3
+    with pytest.raises(vd.VditError) as e:
+        attn.forward(qd, kd, vd_, key_len=10, out=qd)
+    assert e.value.code == 1
+    h = vd.Attention(256, 256, 2, 64)
+    h.close()
+    h.close()  # second close is a no-op on the Python side
