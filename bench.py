@@ -1,0 +1,198 @@
+"""Benchmark: one MI355X, self-attention over one device's Ulysses head share.
+
+Workload: N = 75600 tokens (latent grid 21 x 45 x 80), q/k/v [N, 40, 128] bfloat16
+i.i.d. N(0, 1), heads 0-9 selected (one rank's share at degree 4), d = 128,
+scale 1/sqrt(128), non-causal, no mask, no RoPE. Inputs are resident in HBM
+before timing. One step = the whole hot path through the C ABI: vdit_attn_prepare
+(v -> float16 V^T) then vdit_attn_attend (the attention kernel).
+
+Prints one JSON line. ``value`` = 4 * N * N * d * H / step time (TFLOP/s).
+``roofline`` prices the attention kernel alone against the MI355X dense
+bf16/fp16 MFMA peak, with its duration from HIP events on the launch stream.
+``cpu_baseline`` times the float64 oracle on a bounded sample of query rows.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+N_TOK = 21 * 45 * 80
+HEADS_TOTAL, HEAD_BEGIN, HEAD_COUNT, D = 40, 0, 10, 128
+SEED = 1003
+PEAK_TFLOPS = 2500.0          # MI355X dense bf16 / fp16 MFMA
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_n75600_h10_traffic.json")
+KERNEL_SOURCES = ["long_sequence_attention_amd/csrc/attn_fwd.hip", "long_sequence_attention_amd/csrc/common.hpp"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per attention launch from the committed rocprofv3 counter runs,
+    or None if there are none or the kernel source changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(q, k, v, rows_count: int):
+    import oracle
+    import synthetic_inputs as si
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    rows = si.sample_rows(N_TOK, rows_count, SEED)
+    t0 = time.perf_counter()
+    oracle.mha_reference(q, k, v, head_begin=HEAD_BEGIN, head_count=HEAD_COUNT, rows=rows)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * len(rows) * N_TOK * D * HEAD_COUNT
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(rows)} seeded query rows x {HEAD_COUNT} heads against all {N_TOK} keys "
+                      f"(float64 numpy oracle, {dt:.1f} s)"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-rows", type=int, default=512, help="query rows for the oracle timing (0: skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one MI355X only (one device's head share); --gpus {args.gpus} is not supported",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import synthetic_inputs as si
+    import long_sequence_attention_amd as vd
+
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    q = si.normal_bf16((N_TOK, HEADS_TOTAL, D), SEED, si.STREAM_Q)
+    k = si.normal_bf16((N_TOK, HEADS_TOTAL, D), SEED, si.STREAM_K)
+    v = si.normal_bf16((N_TOK, HEADS_TOTAL, D), SEED, si.STREAM_V)
+    up = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    qd, kd, vdd = up(q), up(k), up(v)
+    print(f"inputs ready in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+
+    attn = vd.Attention(N_TOK, N_TOK, HEADS_TOTAL, D, head_begin=HEAD_BEGIN, head_count=HEAD_COUNT)
+    ws = attn.new_workspace(dev)
+    out = torch.empty(attn.out_shape, dtype=torch.bfloat16, device=dev)
+
+    def step():
+        attn.prepare(qd, kd, vdd, workspace=ws)
+        attn.attend(qd, kd, vdd, out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record()
+        attn.prepare(qd, kd, vdd, workspace=ws)
+        ev[i][1].record()
+        attn.attend(qd, kd, vdd, out=out, workspace=ws)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    prep_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    attend_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    step_ms = wall * 1e3 / args.steps
+
+    flops = 4.0 * N_TOK * N_TOK * D * HEAD_COUNT
+    value = flops / (step_ms * 1e-3) / 1e12
+    achieved = flops / (attend_ms * 1e-3) / 1e12
+    traffic = measured_traffic()
+
+    # pack / unpack of one rank's share at its real shape ([18900, 40, 128] <-> [4, 18900, 10, 128])
+    # and at full-sequence scale; bytes moved = read + write
+    pack = {}
+    for n in (N_TOK // 4, N_TOK):
+        x = qd[:n]
+        p = vd.pack_heads(x, 4)
+        vd.unpack_heads(p)
+        torch.cuda.synchronize()
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        reps = 10
+        e0.record()
+        for _ in range(reps):
+            vd.pack_heads(x, 4, out=p)
+        e1.record()
+        y = torch.empty_like(x)
+        for _ in range(reps):
+            vd.unpack_heads(p, out=y)
+        e2.record()
+        torch.cuda.synchronize()
+        nbytes = 2.0 * x.numel() * 2
+        pack[f"pack_GBps_n{n}"] = round(nbytes / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9, 1)
+        pack[f"unpack_GBps_n{n}"] = round(nbytes / (e1.elapsed_time(e2) / reps * 1e-3) / 1e9, 1)
+        assert torch.equal(y.view(torch.int16), x.view(torch.int16))
+
+    result = {
+        "metric": "attention TFLOP/s + % bf16 MFMA peak at N=75600,H=10,d=128 (1 GPU)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "self-attention, one Ulysses head share: N=75600 (21x45x80), heads 0-9 of 40, d=128, "
+                        "non-causal, no mask, no RoPE, q/k/v bf16 N(0,1) seed 1003",
+            "seq_len": N_TOK, "heads": HEAD_COUNT, "head_dim": D, "qk_dtype": "bf16", "pv_dtype": "fp16",
+            "pct_of_peak": round(100.0 * value / PEAK_TFLOPS, 2),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_TFLOPS, 4),
+            "traffic": traffic,
+        },
+        "kernels": {
+            "attend_ms": round(attend_ms, 4),
+            "prepare_ms": round(prep_ms, 4),
+            "prepare_GBps": round((2 * N_TOK * HEAD_COUNT * D * 2) / (prep_ms * 1e-3) / 1e9, 1),
+            **pack,
+        },
+    }
+    if args.cpu_rows > 0:
+        result["cpu_baseline"] = cpu_baseline(q, k, v, args.cpu_rows)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

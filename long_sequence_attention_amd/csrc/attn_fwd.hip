@@ -1,6 +1,6 @@
 // Flash-style attention forward for gfx950 (CDNA4), bf16 q/k, fp16 weights and v.
 //
-// Work split: one workgroup = 4 waves = BLOCK_M = 4 * QB * 32 queries of one head;
+// Work split: one workgroup = WAVES waves = BLOCK_M = WAVES * QB * 32 queries of one head;
 // it streams all valid keys of that head in tiles of 64 keys through a double-
 // buffered LDS stage (K tile row-major, V^T tile prepared in the workspace).
 //
@@ -24,9 +24,9 @@
 namespace vdit {
 namespace {
 
-template <int D, int QB>
+template <int D, int QB, int WAVES>
 struct FwdCfg {
-  static constexpr int kWaves = 4;
+  static constexpr int kWaves = WAVES;
   static constexpr int kThreads = kWaves * kWave;
   static constexpr int kBlockM = kWaves * QB * 32;
   static constexpr int kKChunks = D / 8;                          // 16-byte chunks per K row
@@ -41,11 +41,9 @@ struct FwdCfg {
   static_assert(kKLoads >= 1 && kVLoads >= 1, "tile too small for the workgroup");
 };
 
-constexpr float kRescaleLog2 = 8.0f;
-
-template <int D, int QB, bool ROPE>
-__global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
-  using C = FwdCfg<D, QB>;
+template <int D, int QB, int WAVES, bool ROPE>
+__global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
+  using C = FwdCfg<D, QB, WAVES>;
   __shared__ __attribute__((aligned(16))) char lds[C::kLds];
 
   // Workgroups are dispatched round-robin over the 8 XCDs; renumber them so that
@@ -88,20 +86,14 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
     }
   }
 
-  f32x16 o[QB][C::kDB];
-  float m_run[QB], l_run[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = -__builtin_inff();
-    l_run[qb] = 0.0f;
-#pragma unroll
-    for (int db = 0; db < C::kDB; ++db) o[qb][db] = f32x16{};
-  }
+  __shared__ int wg_retry;
+  if (tid == 0) wg_retry = 0;
 
   const __bf16* kbase = a.k + (int64_t)head * a.k_head;
   const _Float16* vbase = a.vt + (int64_t)head * a.vt_head;
   const int kv_len = a.kv_len;
   const int ntiles = (kv_len + kBlockN - 1) / kBlockN;
+  const float c = a.c;
 
   u32x4 kreg[C::kKLoads], vreg[C::kVLoads];
   auto gload = [&](int t) {
@@ -110,8 +102,10 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
       const int qd = i * C::kThreads + tid;
       const int row = qd / C::kKChunks;
       const int ch = qd % C::kKChunks;
-      const int key = t * kBlockN + row;
-      kreg[i] = key < kv_len ? *reinterpret_cast<const u32x4*>(kbase + (int64_t)key * a.k_row + ch * 8) : u32x4{};
+      // keys past kv_len read the last valid row instead (their scores are masked),
+      // so no row at or beyond kv_len is ever read
+      const int key = min(t * kBlockN + row, kv_len - 1);
+      kreg[i] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)key * a.k_row + ch * 8);
     }
     const _Float16* vt = vbase + (int64_t)t * (D * kBlockN);
 #pragma unroll
@@ -145,19 +139,9 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
   const int krow_off = l32 * (D * 2);
   const int vrow_off = l32 * (kBlockN * 2);
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int st = t & 1;
-    const bool more = t + 1 < ntiles;
-    if (more) gload(t + 1);
+  // S^T = K * Q^T for the tile in LDS stage `st`, keys past kv_len set to -inf
+  auto scores = [&](int st, int t, f32x16 (&s)[QB][2]) {
     const char* kl = lds + st * C::kStage;
-    const char* vl = kl + C::kKTile;
-
-    // ---- S^T = K * Q^T
-    f32x16 s[QB][2];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) { s[qb][0] = f32x16{}; s[qb][1] = f32x16{}; }
 #pragma unroll
@@ -171,8 +155,6 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
           s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[qb][kk], s[qb][kb], 0, 0, 0);
       }
     }
-
-    // ---- key mask on the ragged last tile
     if (t == ntiles - 1 && (kv_len & (kBlockN - 1))) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
@@ -184,9 +166,9 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
             if (key >= kv_len) s[qb][kb][r] = -__builtin_inff();
           }
     }
-
-    // ---- online softmax (log2 domain), weights to float16
-    f16x8 pf[QB][4];
+  };
+  // maximum of the scores of each query in the tile (both lane halves), times c
+  auto tile_max = [&](const f32x16 (&s)[QB][2], float (&m)[QB]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float mx = s[qb][0][0];
@@ -195,54 +177,110 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][1][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mt = mx * a.c;
-      if (__any(mt > m_run[qb] + kRescaleLog2)) {
-        const float mn = fmaxf(m_run[qb], mt);
-        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - mn);
-        l_run[qb] *= alpha;
+      m[qb] = mx * c;
+    }
+  };
+
+  // One pass over all key tiles with a fixed reference m (log2 domain): weights
+  // p = 2^(s*c - m) rounded to float16, O^T += V^T * P^T, l += sum of the rounded
+  // weights. Entry: tile 0 is in LDS stage 0. A weight above the float16 range
+  // becomes inf and makes l non-finite, which the caller checks.
+  f32x16 o[QB][C::kDB];
+  float l_run[QB];
+  auto main_pass = [&](const float (&mref)[QB]) {
 #pragma unroll
-        for (int db = 0; db < C::kDB; ++db) o[qb][db] *= alpha;
-        m_run[qb] = mn;
+    for (int qb = 0; qb < QB; ++qb) {
+      l_run[qb] = 0.0f;
+#pragma unroll
+      for (int db = 0; db < C::kDB; ++db) o[qb][db] = f32x16{};
+    }
+    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+    for (int t = 0; t < ntiles; ++t) {
+      const int st = t & 1;
+      const bool more = t + 1 < ntiles;
+      if (more) gload(t + 1);
+      f32x16 s[QB][2];
+      scores(st, t, s);
+      f16x8 pf[QB][4];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float nm = -mref[qb];
+        float lsum = 0.0f;
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const int kb = s4 >> 1;
+          const int base = (s4 & 1) * 8;
+          f16x8 pk;
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            f16x2 h2;
+            h2[0] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][base + e], c, nm));
+            h2[1] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][base + e + 1], c, nm));
+            lsum = __builtin_amdgcn_fdot2(h2, ones, lsum, false);
+            pk[e] = h2[0];
+            pk[e + 1] = h2[1];
+          }
+          pf[qb][s4] = pk;
+        }
+        l_run[qb] += lsum;
       }
-      const float nm = -m_run[qb];
-      const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-      float lsum = 0.0f;
+      const char* vl = lds + st * C::kStage + C::kKTile;
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
-        const int kb = s4 >> 1;
-        const int base = (s4 & 1) * 8;
-        f16x8 pk;
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][base + e], a.c, nm));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][base + e + 1], a.c, nm));
-          f16x2 h2;
-          h2[0] = (_Float16)p0;
-          h2[1] = (_Float16)p1;
-          lsum = __builtin_amdgcn_fdot2(h2, ones, lsum, false);
-          pk[e] = h2[0];
-          pk[e + 1] = h2[1];
+        for (int db = 0; db < C::kDB; ++db) {
+          const f16x8 va = *reinterpret_cast<const f16x8*>(
+              vl + db * 32 * (kBlockN * 2) + vrow_off + (((2 * s4 + hl) ^ vswz) << 4));
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf[qb][s4], o[qb][db], 0, 0, 0);
         }
-        pf[qb][s4] = pk;
       }
-      l_run[qb] += lsum;
+      if (more) lstore(st ^ 1);
+      __syncthreads();
     }
+  };
 
-    // ---- O^T += V^T * P^T
+  // ---- reference maximum from the first key tile
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  float mref[QB];
+  {
+    f32x16 s[QB][2];
+    scores(0, 0, s);
+    tile_max(s, mref);
+  }
+  main_pass(mref);
+
+  // ---- rare path: some weight left the float16 range (a later key scored far
+  // above the first tile's maximum) or the inputs were not finite. The whole
+  // workgroup recomputes with the exact row maximum, so no weight exceeds 1.
+  bool bad = false;
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
+  for (int qb = 0; qb < QB; ++qb) bad |= !__builtin_isfinite(l_run[qb]);
+  if (__any(bad) && lane == 0) wg_retry = 1;
+  __syncthreads();
+  if (wg_retry) {
+    float mx[QB];
 #pragma unroll
-      for (int db = 0; db < C::kDB; ++db) {
-        const f16x8 va = *reinterpret_cast<const f16x8*>(
-            vl + db * 32 * (kBlockN * 2) + vrow_off + (((2 * s4 + hl) ^ vswz) << 4));
+    for (int qb = 0; qb < QB; ++qb) mx[qb] = -__builtin_inff();
+    for (int t = 0; t < ntiles; ++t) {
+      gload(t);
+      lstore(0);
+      __syncthreads();
+      f32x16 s[QB][2];
+      scores(0, t, s);
+      float m[QB];
+      tile_max(s, m);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf[qb][s4], o[qb][db], 0, 0, 0);
-      }
+      for (int qb = 0; qb < QB; ++qb) mx[qb] = fmaxf(mx[qb], m[qb]);
+      __syncthreads();
     }
-
-    if (more) lstore(st ^ 1);
+    gload(0);
+    lstore(0);
     __syncthreads();
+    main_pass(mx);
   }
 
   // ---- epilogue: normalise, round to bf16, store [nq, hc, d]
@@ -266,21 +304,21 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
   }
 }
 
-template <int D, int QB, bool ROPE>
+template <int D, int QB, int WAVES, bool ROPE>
 hipError_t launch_fwd_t(AttnArgs a, hipStream_t s) {
-  using C = FwdCfg<D, QB>;
+  using C = FwdCfg<D, QB, WAVES>;
   a.n_qtiles = (a.nq + C::kBlockM - 1) / C::kBlockM;
   const int64_t nwg = (int64_t)a.n_qtiles * a.hc;
   if (nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, QB, ROPE>), dim3((unsigned)nwg), dim3(C::kThreads), 0, s, a);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, QB, WAVES, ROPE>), dim3((unsigned)nwg), dim3(C::kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attn_fwd(const AttnArgs& a, int head_dim, bool rope_q, hipStream_t s) {
-  if (head_dim == 128) return rope_q ? launch_fwd_t<128, 2, true>(a, s) : launch_fwd_t<128, 2, false>(a, s);
-  if (head_dim == 64) return rope_q ? launch_fwd_t<64, 2, true>(a, s) : launch_fwd_t<64, 2, false>(a, s);
+  if (head_dim == 128) return rope_q ? launch_fwd_t<128, 1, 8, true>(a, s) : launch_fwd_t<128, 1, 8, false>(a, s);
+  if (head_dim == 64) return rope_q ? launch_fwd_t<64, 1, 8, true>(a, s) : launch_fwd_t<64, 1, 8, false>(a, s);
   return hipErrorInvalidValue;
 }
 

@@ -352,3 +352,21 @@ def test_call_errors(dev):
     h = vd.Attention(256, 256, 2, 64)
     h.close()
     h.close()  # second close is a no-op on the Python side
+
+
+# ---------------------------------------------------------------------------
+# The exact-maximum retry: scores that grow far past the first key tile's maximum
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("nk,L", [(512, None), (700, 650), (2000, None)])
+def test_scores_growing_past_first_tile_max(dev, nk, L):
+    # key j has k[j, 0] ~ j / 8 and queries have q[:, 0] = 8, so the score of the
+    # last keys exceeds the first tile's maximum by far more than the float16 range
+    nq, ht, d = 300, 2, 128
+    q, k, v = nhd_inputs(nq, nk, ht, d, 9100 + nk, 0.25)
+    q[:, :, 0] = si.f32_to_bf16_bits(np.full((nq, ht), 8.0, dtype=np.float32))
+    ramp = (np.arange(nk, dtype=np.float32) / 8.0)[:, None]
+    k[:, :, 0] = si.f32_to_bf16_bits(np.broadcast_to(ramp, (nk, ht)))
+    q[::7, 1, 0] = si.f32_to_bf16_bits(np.zeros(len(range(0, nq, 7)), dtype=np.float32))  # some rows stay tame
+    out = run_nhd(dev, q, k, v, key_len=L)
+    check(as_f64(out), oracle.mha_reference(q, k, v, key_len=L), f"growing scores nk={nk} L={L}")
