@@ -1,50 +1,67 @@
 // Flash-style attention forward for gfx950 (CDNA4), bf16 q/k, fp16 weights and v.
 //
-// Work split: one workgroup = WAVES waves = BLOCK_M = WAVES * QB * 32 queries of one head;
-// it streams all valid keys of that head in tiles of 64 keys through a double-
-// buffered LDS stage (K tile row-major, V^T tile prepared in the workspace).
+// Work split: one workgroup = WAVES waves = BLOCK_M = WAVES * QB * 32 queries of one
+// head; it streams all valid keys of that head in tiles of 64 keys. K tiles (row-
+// major, from the input or the rotated-key workspace) and V^T tiles (prepared in
+// the workspace) reach LDS by direct global->LDS loads (global_load_lds_dwordx4),
+// double-buffered in four distinct LDS arrays.
 //
 // Per wave and key tile the scores are formed transposed, S^T = K * Q^T, with
 // v_mfma_f32_32x32x16_bf16: the A operand is a 32-key x 16-dim slice of K read
 // from LDS, the B operand is the wave's queries held in registers for the whole
 // loop. In the 32x32 accumulator layout lane l holds query (l % 32) and 16 of
-// its keys, the other 16 in lane l ^ 32, so the per-query maximum and sum need
-// one cross-half exchange only. The float16 weights P^T stay in the same lanes
-// and serve directly as the B operand of O^T += V^T * P^T
+// its keys, the other 16 in lane l ^ 32. The float16 weights P^T stay in the
+// same lanes and serve directly as the B operand of O^T += V^T * P^T
 // (v_mfma_f32_32x32x16_f16); the workspace stores V^T with the key order inside
 // each group of 16 permuted (bits 2 and 3 of the key index swapped) so that the
 // A operand for a lane is one 16-byte LDS read.
 //
-// Softmax runs in the log2 domain (c = scale * log2 e) with a running maximum
-// that is only raised when a tile's maximum exceeds it by more than 2^8, so the
-// rescale of O is rare after the first tiles; the row sum is taken from the
-// rounded float16 weights (v_dot2), the same values the product uses.
+// Softmax: the weights use a fixed reference, the row maximum of the first key
+// tile, in the log2 domain (c = scale * log2 e): p = 2^(s*c - m). O is never
+// rescaled. If some later score exceeds the reference by more than the float16
+// range allows, a weight becomes inf and the row sum non-finite; the workgroup
+// then recomputes its rows with the exact row maximum. The row sum is taken from
+// the rounded float16 weights (v_dot2), the same values the product uses.
 #include "common.hpp"
 
 namespace vdit {
 namespace {
+
+// 16 bytes per lane from global memory straight into LDS: lane l of the wave
+// writes [lds + 16 l, lds + 16 l + 16). `lds` must be the same for the whole wave.
+__device__ __forceinline__ void dma16(const void* g, char* lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
 
 template <int D, int QB, int WAVES>
 struct FwdCfg {
   static constexpr int kWaves = WAVES;
   static constexpr int kThreads = kWaves * kWave;
   static constexpr int kBlockM = kWaves * QB * 32;
-  static constexpr int kKChunks = D / 8;                          // 16-byte chunks per K row
-  static constexpr int kKTile = kBlockN * D * 2;                   // bytes
-  static constexpr int kVTile = D * kBlockN * 2;                   // bytes
-  static constexpr int kStage = kKTile + kVTile;
-  static constexpr int kLds = 2 * kStage;
-  static constexpr int kKLoads = kBlockN * kKChunks / kThreads;    // 16-byte loads per thread
-  static constexpr int kVLoads = D * (kBlockN / 8) / kThreads;
-  static constexpr int kDK = D / 16;                               // MFMA k-steps over d
-  static constexpr int kDB = D / 32;                               // 32-row blocks of d
-  static_assert(kKLoads >= 1 && kVLoads >= 1, "tile too small for the workgroup");
+  static constexpr int kKChunks = D / 8;                 // 16-byte chunks per K row
+  static constexpr int kKRow = D * 2;                    // bytes per K row in LDS
+  static constexpr int kVRow = kBlockN * 2;              // bytes per V^T row in LDS
+  static constexpr int kKTile = kBlockN * kKRow;         // bytes
+  static constexpr int kVTile = D * kVRow;               // bytes
+  static constexpr int kKDma = kKTile / 1024 / kWaves;   // 1 KB direct loads per wave per K tile
+  static constexpr int kVDma = kVTile / 1024 / kWaves;
+  static constexpr int kDK = D / 16;                     // MFMA k-steps over d
+  static constexpr int kDB = D / 32;                     // 32-row blocks of d
+  static_assert(kKDma >= 1 && kVDma >= 1 && kKDma * kWaves * 1024 == kKTile && kVDma * kWaves * 1024 == kVTile,
+                "tiles must split into whole 1 KB direct loads per wave");
 };
 
 template <int D, int QB, int WAVES, bool ROPE>
 __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   using C = FwdCfg<D, QB, WAVES>;
-  __shared__ __attribute__((aligned(16))) char lds[C::kLds];
+  // Four distinct arrays (not one array indexed by stage) so that the compiler
+  // can tell a direct load into one stage from reads of another and only waits
+  // for the direct loads at the barriers.
+  __shared__ __attribute__((aligned(1024))) char k_st0[C::kKTile];
+  __shared__ __attribute__((aligned(1024))) char k_st1[C::kKTile];
+  __shared__ __attribute__((aligned(1024))) char v_st0[C::kVTile];
+  __shared__ __attribute__((aligned(1024))) char v_st1[C::kVTile];
+  __shared__ int wg_retry;
 
   // Workgroups are dispatched round-robin over the 8 XCDs; renumber them so that
   // each XCD walks a contiguous range of (head, query tile) and its L2 serves the
@@ -64,7 +81,9 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   const int l32 = lane & 31;
   const int hl = lane >> 5;
 
-  // ---- prologue: this wave's queries into registers (B operand layout), RoPE fused
+  if (tid == 0) wg_retry = 0;
+
+  // ---- this wave's queries into registers (B operand layout), RoPE fused
   const int q0 = qtile * C::kBlockM + wave * QB * 32;
   bf16x8 qf[QB][C::kDK];
 #pragma unroll
@@ -86,62 +105,61 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
     }
   }
 
-  __shared__ int wg_retry;
-  if (tid == 0) wg_retry = 0;
-
-  const __bf16* kbase = a.k + (int64_t)head * a.k_head;
-  const _Float16* vbase = a.vt + (int64_t)head * a.vt_head;
   const int kv_len = a.kv_len;
   const int ntiles = (kv_len + kBlockN - 1) / kBlockN;
   const float c = a.c;
+  const char* kbytes = reinterpret_cast<const char*>(a.k + (int64_t)head * a.k_head);
+  const char* vbytes = reinterpret_cast<const char*>(a.vt + (int64_t)head * a.vt_head);
+  const int krow_bytes = (int)(a.k_row * 2);
 
-  u32x4 kreg[C::kKLoads], vreg[C::kVLoads];
-  auto gload = [&](int t) {
+  // ---- direct global -> LDS staging. Wave w fills the 1 KB pieces w*n .. w*n+n-1
+  // of a tile; lane l writes bytes [16 l, 16 l + 16) of a piece, i.e. the LDS
+  // position (row, physical chunk) that the XOR swizzle assigns to a logical
+  // (row, chunk) of the tile, so each lane fetches that logical chunk.
+  int kdma_row[C::kKDma], kdma_off[C::kKDma], vdma_off[C::kVDma];
 #pragma unroll
-    for (int i = 0; i < C::kKLoads; ++i) {
-      const int qd = i * C::kThreads + tid;
-      const int row = qd / C::kKChunks;
-      const int ch = qd % C::kKChunks;
-      // keys past kv_len read the last valid row instead (their scores are masked),
-      // so no row at or beyond kv_len is ever read
-      const int key = min(t * kBlockN + row, kv_len - 1);
-      kreg[i] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)key * a.k_row + ch * 8);
-    }
-    const _Float16* vt = vbase + (int64_t)t * (D * kBlockN);
+  for (int i = 0; i < C::kKDma; ++i) {
+    const int byte = (wave * C::kKDma + i) * 1024 + lane * 16;
+    const int row = byte / C::kKRow;
+    const int pc = (byte % C::kKRow) / 16;
+    kdma_row[i] = row;
+    kdma_off[i] = (pc ^ (row & (C::kKChunks - 1))) * 16;
+  }
 #pragma unroll
-    for (int i = 0; i < C::kVLoads; ++i) {
-      const int qd = i * C::kThreads + tid;
-      vreg[i] = *reinterpret_cast<const u32x4*>(vt + qd * 8);
+  for (int i = 0; i < C::kVDma; ++i) {
+    const int byte = (wave * C::kVDma + i) * 1024 + lane * 16;
+    const int row = byte / C::kVRow;
+    const int pc = (byte % C::kVRow) / 16;
+    vdma_off[i] = row * C::kVRow + (pc ^ ((row >> 1) & 7)) * 16;
+  }
+  // K rows past kv_len re-read the last valid row (their scores are masked), so
+  // no row at or beyond kv_len is ever read; tiles past the last one re-read it.
+  auto dma_k = [&](int t, char* st) {
+    t = min(t, ntiles - 1);
+    const char* kt = kbytes + (int64_t)t * kBlockN * krow_bytes;
+    const int lim = kv_len - 1 - t * kBlockN;
+#pragma unroll
+    for (int i = 0; i < C::kKDma; ++i) {
+      const int row = min(kdma_row[i], lim);
+      dma16(kt + (uint32_t)(row * krow_bytes + kdma_off[i]), st + (wave * C::kKDma + i) * 1024);
     }
   };
-  auto lstore = [&](int stage) {
-    char* kl = lds + stage * C::kStage;
-    char* vl = kl + C::kKTile;
+  auto dma_v = [&](int t, char* st) {
+    t = min(t, ntiles - 1);
+    const char* vt = vbytes + (int64_t)t * C::kVTile;
 #pragma unroll
-    for (int i = 0; i < C::kKLoads; ++i) {
-      const int qd = i * C::kThreads + tid;
-      const int row = qd / C::kKChunks;
-      const int ch = qd % C::kKChunks;
-      *reinterpret_cast<u32x4*>(kl + row * (D * 2) + ((ch ^ (row & (C::kKChunks - 1))) << 4)) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < C::kVLoads; ++i) {
-      const int qd = i * C::kThreads + tid;
-      const int row = qd >> 3;
-      const int ch = qd & 7;
-      *reinterpret_cast<u32x4*>(vl + row * (kBlockN * 2) + ((ch ^ ((row >> 1) & 7)) << 4)) = vreg[i];
-    }
+    for (int i = 0; i < C::kVDma; ++i)
+      dma16(vt + vdma_off[i], st + (wave * C::kVDma + i) * 1024);
   };
 
   // per-lane LDS read offsets (the XOR swizzle only depends on the lane)
   const int kswz = l32 & (C::kKChunks - 1);
   const int vswz = (l32 >> 1) & 7;
-  const int krow_off = l32 * (D * 2);
-  const int vrow_off = l32 * (kBlockN * 2);
+  const int krow_off = l32 * C::kKRow;
+  const int vrow_off = l32 * C::kVRow;
 
-  // S^T = K * Q^T for the tile in LDS stage `st`, keys past kv_len set to -inf
-  auto scores = [&](int st, int t, f32x16 (&s)[QB][2]) {
-    const char* kl = lds + st * C::kStage;
+  // S^T = K * Q^T for the K tile in `kl`
+  auto scores = [&](const char* kl, f32x16 (&s)[QB][2]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) { s[qb][0] = f32x16{}; s[qb][1] = f32x16{}; }
 #pragma unroll
@@ -149,13 +167,17 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const bf16x8 ka = *reinterpret_cast<const bf16x8*>(
-            kl + kb * 32 * (D * 2) + krow_off + (((2 * kk + hl) ^ kswz) << 4));
+            kl + kb * 32 * C::kKRow + krow_off + (((2 * kk + hl) ^ kswz) << 4));
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[qb][kk], s[qb][kb], 0, 0, 0);
       }
     }
-    if (t == ntiles - 1 && (kv_len & (kBlockN - 1))) {
+  };
+  // scores of keys past kv_len to -inf (only the last tile can hold such keys)
+  const bool ragged = (kv_len & (kBlockN - 1)) != 0;
+  auto mask_tail = [&](int t, f32x16 (&s)[QB][2]) {
+    if (t == ntiles - 1 && ragged) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -181,12 +203,81 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
     }
   };
 
-  // One pass over all key tiles with a fixed reference m (log2 domain): weights
-  // p = 2^(s*c - m) rounded to float16, O^T += V^T * P^T, l += sum of the rounded
-  // weights. Entry: tile 0 is in LDS stage 0. A weight above the float16 range
-  // becomes inf and makes l non-finite, which the caller checks.
+  // Weights p = 2^(s*c - m) for the reference m, rounded to float16, and
+  // l += their sum. A weight above the float16 range becomes inf.
   f32x16 o[QB][C::kDB];
   float l_run[QB];
+  const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+  auto weights = [&](const f32x16 (&s)[QB][2], const float (&mref)[QB], f16x8 (&pf)[QB][4]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float nm = -mref[qb];
+      float lsum[4];
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const int kb = s4 >> 1;
+        const int base = (s4 & 1) * 8;
+        u32x4 bits;
+        lsum[s4] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          f16x2 h2;
+          h2[0] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][base + 2 * e], c, nm));
+          h2[1] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][base + 2 * e + 1], c, nm));
+          lsum[s4] = __builtin_amdgcn_fdot2(h2, ones, lsum[s4], false);
+          bits[e] = __builtin_bit_cast(uint32_t, h2);
+        }
+        pf[qb][s4] = __builtin_bit_cast(f16x8, bits);
+      }
+      l_run[qb] += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+    }
+  };
+  // O^T += V^T * P^T with the V^T tile in `vl`
+  auto products = [&](const char* vl, const f16x8 (&pf)[QB][4]) {
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+#pragma unroll
+      for (int db = 0; db < C::kDB; ++db) {
+        const f16x8 va = *reinterpret_cast<const f16x8*>(
+            vl + db * 32 * C::kVRow + vrow_off + (((2 * s4 + hl) ^ vswz) << 4));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf[qb][s4], o[qb][db], 0, 0, 0);
+      }
+    }
+  };
+
+  // Stage tiles 0 (K and V) and 1 (K only) and form the scores of tile 0.
+  f32x16 s_a[QB][2], s_b[QB][2];
+  auto prologue = [&]() {
+    dma_k(0, k_st0);
+    dma_v(0, v_st0);
+    dma_k(1, k_st1);
+    __syncthreads();
+    scores(k_st0, s_a);
+    mask_tail(0, s_a);
+  };
+
+  // One software-pipelined pass over all key tiles. In iteration t each wave
+  // forms the scores of tile t+1 (MFMA) while it turns the held scores of tile t
+  // into weights (VALU): the two are independent and sit in one branch-free
+  // region, so the matrix and vector units work at the same time. Then
+  // O += V^T(t) P^T(t). K therefore runs one tile ahead of V in LDS: iteration t
+  // reads K stage (t+1) & 1 and V stage t & 1, and the direct loads of K(t+2)
+  // and V(t+1) fill the other two, which nobody reads in it. Staging indices past
+  // the last tile re-stage the last tile, and the last iteration also forms
+  // scores it does not use, so the control flow of every iteration is the same.
+  auto step = [&](int t, char* k_read, char* k_fill, char* v_read, char* v_fill, f32x16 (&s_cur)[QB][2],
+                  f32x16 (&s_next)[QB][2], const float (&mref)[QB]) {
+    dma_k(t + 2, k_fill);
+    dma_v(t + 1, v_fill);
+    f16x8 pf[QB][4];
+    scores(k_read, s_next);
+    weights(s_cur, mref, pf);
+    products(v_read, pf);
+    mask_tail(t + 1, s_next);
+    __syncthreads();
+  };
   auto main_pass = [&](const float (&mref)[QB]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -194,63 +285,16 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int db = 0; db < C::kDB; ++db) o[qb][db] = f32x16{};
     }
-    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-    for (int t = 0; t < ntiles; ++t) {
-      const int st = t & 1;
-      const bool more = t + 1 < ntiles;
-      if (more) gload(t + 1);
-      f32x16 s[QB][2];
-      scores(st, t, s);
-      f16x8 pf[QB][4];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const float nm = -mref[qb];
-        float lsum = 0.0f;
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-          const int kb = s4 >> 1;
-          const int base = (s4 & 1) * 8;
-          f16x8 pk;
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            f16x2 h2;
-            h2[0] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][base + e], c, nm));
-            h2[1] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][base + e + 1], c, nm));
-            lsum = __builtin_amdgcn_fdot2(h2, ones, lsum, false);
-            pk[e] = h2[0];
-            pk[e + 1] = h2[1];
-          }
-          pf[qb][s4] = pk;
-        }
-        l_run[qb] += lsum;
-      }
-      const char* vl = lds + st * C::kStage + C::kKTile;
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-#pragma unroll
-        for (int db = 0; db < C::kDB; ++db) {
-          const f16x8 va = *reinterpret_cast<const f16x8*>(
-              vl + db * 32 * (kBlockN * 2) + vrow_off + (((2 * s4 + hl) ^ vswz) << 4));
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf[qb][s4], o[qb][db], 0, 0, 0);
-        }
-      }
-      if (more) lstore(st ^ 1);
-      __syncthreads();
+    for (int t = 0; t < ntiles; t += 2) {
+      step(t, k_st1, k_st0, v_st0, v_st1, s_a, s_b, mref);
+      if (t + 1 < ntiles) step(t + 1, k_st0, k_st1, v_st1, v_st0, s_b, s_a, mref);
     }
   };
 
   // ---- reference maximum from the first key tile
-  gload(0);
-  lstore(0);
-  __syncthreads();
+  prologue();
   float mref[QB];
-  {
-    f32x16 s[QB][2];
-    scores(0, 0, s);
-    tile_max(s, mref);
-  }
+  tile_max(s_a, mref);
   main_pass(mref);
 
   // ---- rare path: some weight left the float16 range (a later key scored far
@@ -266,20 +310,18 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) mx[qb] = -__builtin_inff();
     for (int t = 0; t < ntiles; ++t) {
-      gload(t);
-      lstore(0);
+      dma_k(t, k_st0);
       __syncthreads();
       f32x16 s[QB][2];
-      scores(0, t, s);
+      scores(k_st0, s);
+      mask_tail(t, s);
       float m[QB];
       tile_max(s, m);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) mx[qb] = fmaxf(mx[qb], m[qb]);
       __syncthreads();
     }
-    gload(0);
-    lstore(0);
-    __syncthreads();
+    prologue();
     main_pass(mx);
   }
 
