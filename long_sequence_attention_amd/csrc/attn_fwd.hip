@@ -27,10 +27,34 @@
 namespace vdit {
 namespace {
 
-// 16 bytes per lane from global memory straight into LDS: lane l of the wave
-// writes [lds + 16 l, lds + 16 l + 16). `lds` must be the same for the whole wave.
-__device__ __forceinline__ void dma16(const void* g, char* lds) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+// 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4):
+// lane l of the wave writes LDS bytes [lds + 16 l, lds + 16 l + 16); `lds` is an
+// LDS byte address, the same for the whole wave. Written as inline assembly so
+// that the compiler does not track these loads: every wait for them is explicit
+// (wait_vm), which lets loads for later tiles stay in flight across barriers.
+// The statement has no register outputs; the LDS address is an M0 input.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
+}
+
+// s_waitcnt vmcnt(N): all but the newest N vector-memory loads of this wave have
+// completed (loads complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// workgroup barrier that the compiler may not move LDS accesses across; it
+// waits for nothing by itself
+__device__ __forceinline__ void barrier_only() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
 }
 
 template <int D, int QB, int WAVES>
@@ -54,13 +78,17 @@ struct FwdCfg {
 template <int D, int QB, int WAVES, bool ROPE>
 __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   using C = FwdCfg<D, QB, WAVES>;
-  // Four distinct arrays (not one array indexed by stage) so that the compiler
-  // can tell a direct load into one stage from reads of another and only waits
-  // for the direct loads at the barriers.
+  // Four K and four V^T stages, each its own array (not one array indexed by
+  // stage) so that the compiler can tell a direct load into one stage from
+  // reads of another and does not wait for the direct loads before LDS reads.
   __shared__ __attribute__((aligned(1024))) char k_st0[C::kKTile];
   __shared__ __attribute__((aligned(1024))) char k_st1[C::kKTile];
+  __shared__ __attribute__((aligned(1024))) char k_st2[C::kKTile];
+  __shared__ __attribute__((aligned(1024))) char k_st3[C::kKTile];
   __shared__ __attribute__((aligned(1024))) char v_st0[C::kVTile];
   __shared__ __attribute__((aligned(1024))) char v_st1[C::kVTile];
+  __shared__ __attribute__((aligned(1024))) char v_st2[C::kVTile];
+  __shared__ __attribute__((aligned(1024))) char v_st3[C::kVTile];
   __shared__ int wg_retry;
 
   // Workgroups are dispatched round-robin over the 8 XCDs; renumber them so that
@@ -134,29 +162,35 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   }
   // K rows past kv_len re-read the last valid row (their scores are masked), so
   // no row at or beyond kv_len is ever read; tiles past the last one re-read it.
-  auto dma_k = [&](int t, char* st) {
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto dma_k = [&](int t, const char* st) {
     t = min(t, ntiles - 1);
     const char* kt = kbytes + (int64_t)t * kBlockN * krow_bytes;
     const int lim = kv_len - 1 - t * kBlockN;
 #pragma unroll
     for (int i = 0; i < C::kKDma; ++i) {
       const int row = min(kdma_row[i], lim);
-      dma16(kt + (uint32_t)(row * krow_bytes + kdma_off[i]), st + (wave * C::kKDma + i) * 1024);
+      dma16(kt + (uint32_t)(row * krow_bytes + kdma_off[i]), lds_addr(st) + (wave_u * C::kKDma + i) * 1024);
     }
   };
-  auto dma_v = [&](int t, char* st) {
+  auto dma_v = [&](int t, const char* st) {
     t = min(t, ntiles - 1);
     const char* vt = vbytes + (int64_t)t * C::kVTile;
 #pragma unroll
-    for (int i = 0; i < C::kVDma; ++i)
-      dma16(vt + vdma_off[i], st + (wave * C::kVDma + i) * 1024);
+    for (int i = 0; i < C::kVDma; ++i) dma16(vt + vdma_off[i], lds_addr(st) + (wave_u * C::kVDma + i) * 1024);
   };
 
-  // per-lane LDS read offsets (the XOR swizzle only depends on the lane)
-  const int kswz = l32 & (C::kKChunks - 1);
-  const int vswz = (l32 >> 1) & 7;
-  const int krow_off = l32 * C::kKRow;
-  const int vrow_off = l32 * C::kVRow;
+  // per-lane LDS read offsets: the XOR swizzle depends only on the lane and the
+  // k-step, so the stage base and the 32-row block fold into the immediate offset
+  int koff[C::kDK], voff[4];
+  {
+    const int kswz = l32 & (C::kKChunks - 1);
+    const int vswz = (l32 >> 1) & 7;
+#pragma unroll
+    for (int kk = 0; kk < C::kDK; ++kk) koff[kk] = l32 * C::kKRow + (((2 * kk + hl) ^ kswz) << 4);
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) voff[s4] = l32 * C::kVRow + (((2 * s4 + hl) ^ vswz) << 4);
+  }
 
   // S^T = K * Q^T for the K tile in `kl`
   auto scores = [&](const char* kl, f32x16 (&s)[QB][2]) {
@@ -166,8 +200,7 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
     for (int kk = 0; kk < C::kDK; ++kk) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(
-            kl + kb * 32 * C::kKRow + krow_off + (((2 * kk + hl) ^ kswz) << 4));
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kl + kb * 32 * C::kKRow + koff[kk]);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[qb][kk], s[qb][kb], 0, 0, 0);
@@ -178,6 +211,8 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   const bool ragged = (kv_len & (kBlockN - 1)) != 0;
   auto mask_tail = [&](int t, f32x16 (&s)[QB][2]) {
     if (t == ntiles - 1 && ragged) {
+      // keeps the compiler from executing this block unconditionally with selects
+      asm volatile("");
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -238,8 +273,7 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
     for (int s4 = 0; s4 < 4; ++s4) {
 #pragma unroll
       for (int db = 0; db < C::kDB; ++db) {
-        const f16x8 va = *reinterpret_cast<const f16x8*>(
-            vl + db * 32 * C::kVRow + vrow_off + (((2 * s4 + hl) ^ vswz) << 4));
+        const f16x8 va = *reinterpret_cast<const f16x8*>(vl + db * 32 * C::kVRow + voff[s4]);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf[qb][s4], o[qb][db], 0, 0, 0);
@@ -247,36 +281,50 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
     }
   };
 
-  // Stage tiles 0 (K and V) and 1 (K only) and form the scores of tile 0.
+  // direct loads issued per iteration by one wave
+  constexpr int kPerIter = C::kKDma + C::kVDma;
+
+  // Stage tiles 0..2 (V) and 0..3 (K) and form the scores of tile 0.
   f32x16 s_a[QB][2], s_b[QB][2];
   auto prologue = [&]() {
     dma_k(0, k_st0);
     dma_v(0, v_st0);
     dma_k(1, k_st1);
-    __syncthreads();
+    dma_v(1, v_st1);
+    dma_k(2, k_st2);
+    dma_v(2, v_st2);
+    dma_k(3, k_st3);
+    wait_vm<0>();
+    barrier_only();
     scores(k_st0, s_a);
     mask_tail(0, s_a);
+    // every wave has read stage 0 before iteration 0 refills it
+    barrier_only();
   };
 
   // One software-pipelined pass over all key tiles. In iteration t each wave
   // forms the scores of tile t+1 (MFMA) while it turns the held scores of tile t
   // into weights (VALU): the two are independent and sit in one branch-free
   // region, so the matrix and vector units work at the same time. Then
-  // O += V^T(t) P^T(t). K therefore runs one tile ahead of V in LDS: iteration t
-  // reads K stage (t+1) & 1 and V stage t & 1, and the direct loads of K(t+2)
-  // and V(t+1) fill the other two, which nobody reads in it. Staging indices past
-  // the last tile re-stage the last tile, and the last iteration also forms
-  // scores it does not use, so the control flow of every iteration is the same.
+  // O += V^T(t) P^T(t). Iteration t reads K stage (t+1) % 4 and V stage t % 4 and
+  // issues the direct loads of K(t+4) and V(t+3) into stages t % 4 and
+  // (t+3) % 4, which nobody reads in it; a load thus has three iterations to
+  // land. Staging indices past the last tile re-stage the last tile, and the last
+  // iteration also forms scores it does not use, so the control flow of every
+  // iteration is the same.
   auto step = [&](int t, char* k_read, char* k_fill, char* v_read, char* v_fill, f32x16 (&s_cur)[QB][2],
                   f32x16 (&s_next)[QB][2], const float (&mref)[QB]) {
-    dma_k(t + 2, k_fill);
-    dma_v(t + 1, v_fill);
+    dma_k(t + 4, k_fill);
+    dma_v(t + 3, v_fill);
     f16x8 pf[QB][4];
     scores(k_read, s_next);
     weights(s_cur, mref, pf);
     products(v_read, pf);
     mask_tail(t + 1, s_next);
-    __syncthreads();
+    // the loads of iteration t-2 (needed in iteration t+1) have landed; those of
+    // iterations t-1 and t stay in flight
+    wait_vm<2 * kPerIter>();
+    barrier_only();
   };
   auto main_pass = [&](const float (&mref)[QB]) {
 #pragma unroll
@@ -285,10 +333,15 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int db = 0; db < C::kDB; ++db) o[qb][db] = f32x16{};
     }
-    for (int t = 0; t < ntiles; t += 2) {
-      step(t, k_st1, k_st0, v_st0, v_st1, s_a, s_b, mref);
-      if (t + 1 < ntiles) step(t + 1, k_st0, k_st1, v_st1, v_st0, s_b, s_a, mref);
+    for (int t = 0; t < ntiles; t += 4) {
+      step(t, k_st1, k_st0, v_st0, v_st3, s_a, s_b, mref);
+      if (t + 1 < ntiles) step(t + 1, k_st2, k_st1, v_st1, v_st0, s_b, s_a, mref);
+      if (t + 2 < ntiles) step(t + 2, k_st3, k_st2, v_st2, v_st1, s_a, s_b, mref);
+      if (t + 3 < ntiles) step(t + 3, k_st0, k_st3, v_st3, v_st2, s_b, s_a, mref);
     }
+    // drain the direct loads still in flight before the stages are reused
+    wait_vm<0>();
+    barrier_only();
   };
 
   // ---- reference maximum from the first key tile
@@ -311,7 +364,8 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
     for (int qb = 0; qb < QB; ++qb) mx[qb] = -__builtin_inff();
     for (int t = 0; t < ntiles; ++t) {
       dma_k(t, k_st0);
-      __syncthreads();
+      wait_vm<0>();
+      barrier_only();
       f32x16 s[QB][2];
       scores(k_st0, s);
       mask_tail(t, s);
