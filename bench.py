@@ -78,7 +78,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-rows", type=int, default=512, help="query rows for the oracle timing (0: skip)")
+    ap.add_argument("--cpu-rows", type=int, default=4096, help="query rows for the oracle timing (0: skip)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one MI355X only (one device's head share); --gpus {args.gpus} is not supported",
