@@ -33,8 +33,13 @@ namespace {
 // that the compiler does not track these loads: every wait for them is explicit
 // (wait_vm), which lets loads for later tiles stay in flight across barriers.
 // The statement has no register outputs; the LDS address is an M0 input.
+// Because the compiler does not see a memory instruction here, it also does not
+// insert the wait states such an instruction needs after its operands are
+// written: the global address therefore comes in VGPRs (dependencies on VGPRs
+// are interlocked by the hardware, unlike an SGPR base written by VALU), and
+// the s_nop covers the one wait state an LDS-DMA load needs after M0 is written.
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
 }
 
 // s_waitcnt vmcnt(N): all but the newest N vector-memory loads of this wave have
