@@ -3,8 +3,8 @@
 // Work split: one workgroup = WAVES waves = BLOCK_M = WAVES * QB * 32 queries of one
 // head; it streams all valid keys of that head in tiles of 64 keys. K tiles (row-
 // major, from the input or the rotated-key workspace) and V^T tiles (prepared in
-// the workspace) reach LDS by direct global->LDS loads (global_load_lds_dwordx4),
-// double-buffered in four distinct LDS arrays.
+// the workspace) reach LDS by direct global->LDS loads (global_load_lds_dwordx4)
+// into four K and four V^T stages, issued four (K) and two (V^T) iterations ahead.
 //
 // Per wave and key tile the scores are formed transposed, S^T = K * Q^T, with
 // v_mfma_f32_32x32x16_bf16: the A operand is a 32-key x 16-dim slice of K read
@@ -15,6 +15,11 @@
 // (v_mfma_f32_32x32x16_f16); the workspace stores V^T with the key order inside
 // each group of 16 permuted (bits 2 and 3 of the key index swapped) so that the
 // A operand for a lane is one 16-byte LDS read.
+//
+// Per iteration a wave forms the scores of the next tile while it turns the held
+// scores into weights, then runs the weight products. The two waves sharing a
+// SIMD are kept half an iteration apart (one forms scores and weights while the
+// other runs products), so the SIMD's matrix and vector units overlap.
 //
 // Softmax: the weights use a fixed reference, the row maximum of the first key
 // tile, in the log2 domain (c = scale * log2 e): p = 2^(s*c - m). O is never
@@ -243,53 +248,116 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
     }
   };
 
-  // Weights p = 2^(s*c - m) for the reference m, rounded to float16, and
-  // l += their sum. A weight above the float16 range becomes inf.
+  // O^T accumulators and row sums of the weights
   f32x16 o[QB][C::kDB];
   float l_run[QB];
   const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-  auto weights = [&](const f32x16 (&s)[QB][2], const float (&mref)[QB], f16x8 (&pf)[QB][4]) {
+
+  // ---- one iteration's matrix and vector work, scheduled by hand. A tile has
+  // kNS score products (k-step j/2, key block j%2) and kNP weight products
+  // (key step j/kDB, d block j%kDB) per 32 queries. LDS fragments are read kR
+  // products ahead into a ring of registers, and each score product is grouped
+  // with its share of the softmax of the previous tile (p = 2^(s*c - m) for the
+  // reference m, rounded to float16; a weight above the float16 range becomes
+  // inf), so a wave has several LDS reads in flight and vector work to issue
+  // while its products run. sched_barrier keeps the compiler from regrouping (it
+  // otherwise trades the read-ahead for registers and waits on every read); the
+  // empty asm statements pin values to their group where the compiler would
+  // otherwise sink their computation into a later block. Per accumulator the
+  // products run in the order of scores() above.
+  constexpr int kNS = 2 * C::kDK;
+  constexpr int kNP = 4 * C::kDB;
+  constexpr int kR = 4;
+  constexpr int kPairs = 16;                 // float16 pairs of weights per lane
+  constexpr int kPPG = kPairs / kNS;         // pairs per score product
+  static_assert(kNS >= kR && kNP >= kR && kPairs % kNS == 0 && kPairs % kNP == 0, "pipeline shape");
+  auto kfrag = [&](const char* kl, int j) {
+    return *reinterpret_cast<const bf16x8*>(kl + (j & 1) * 32 * C::kKRow + koff[j >> 1]);
+  };
+  auto vfrag = [&](const char* vl, int j) {
+    return *reinterpret_cast<const f16x8*>(vl + (j % C::kDB) * 32 * C::kVRow + voff[j / C::kDB]);
+  };
+  // scores of the next tile with the weights of the held one; leaves the first
+  // kR V^T fragments of the products in `vr`
+  auto score_phase = [&](const char* k_read, const char* v_read, const f32x16 (&s_cur)[QB][2],
+                         f32x16 (&s_next)[QB][2], const float (&mref)[QB], f16x8 (&vr)[kR], f16x8 (&pf)[QB][4],
+                         f16x2 (&hv)[QB][kPairs]) {
+    bf16x8 kr[kR];
+    u32x4 bits[QB][4];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const float nm = -mref[qb];
-      float lsum[4];
+      s_next[qb][0] = f32x16{};
+      s_next[qb][1] = f32x16{};
+    }
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        const int kb = s4 >> 1;
-        const int base = (s4 & 1) * 8;
-        u32x4 bits;
-        lsum[s4] = 0.0f;
+    for (int j = 0; j < kR; ++j) kr[j] = kfrag(k_read, j);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+    for (int g = 0; g < kNS; ++g) {
+      const int kk = g >> 1, kb = g & 1;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        s_next[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[g % kR], qf[qb][kk], s_next[qb][kb], 0, 0, 0);
+      if (g + kR < kNS)
+        kr[g % kR] = kfrag(k_read, g + kR);
+      else
+        vr[g + kR - kNS] = vfrag(v_read, g + kR - kNS);
+#pragma unroll
+      for (int p = g * kPPG; p < (g + 1) * kPPG; ++p) {
+        const int s4 = p >> 2, e = p & 3;
+        const int skb = s4 >> 1, r = (s4 & 1) * 8 + 2 * e;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const float nm = -mref[qb];
           f16x2 h2;
-          h2[0] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][base + 2 * e], c, nm));
-          h2[1] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][base + 2 * e + 1], c, nm));
-          lsum[s4] = __builtin_amdgcn_fdot2(h2, ones, lsum[s4], false);
-          bits[e] = __builtin_bit_cast(uint32_t, h2);
+          h2[0] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[qb][skb][r], c, nm));
+          h2[1] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[qb][skb][r + 1], c, nm));
+          uint32_t u = __builtin_bit_cast(uint32_t, h2);
+          asm volatile("" : "+v"(u));  // keeps the weights in this group
+          hv[qb][p] = __builtin_bit_cast(f16x2, u);
+          bits[qb][s4][e] = u;
         }
-        pf[qb][s4] = __builtin_bit_cast(f16x8, bits);
       }
-      l_run[qb] += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+      __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) pf[qb][s4] = __builtin_bit_cast(f16x8, bits[qb][s4]);
   };
-  // O^T += V^T * P^T with the V^T tile in `vl`
-  auto products = [&](const char* vl, const f16x8 (&pf)[QB][4]) {
+  // O^T += V^T P^T; the row sums of the rounded weights (v_dot2) ride along with
+  // the products, which have no other vector work
+  auto product_phase = [&](const char* v_read, f16x8 (&vr)[kR], const f16x8 (&pf)[QB][4],
+                           const f16x2 (&hv)[QB][kPairs]) {
+    float lsum[QB][4];
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int db = 0; db < C::kDB; ++db) {
-        const f16x8 va = *reinterpret_cast<const f16x8*>(vl + db * 32 * C::kVRow + voff[s4]);
+      for (int s4 = 0; s4 < 4; ++s4) lsum[qb][s4] = 0.0f;
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf[qb][s4], o[qb][db], 0, 0, 0);
-      }
+    for (int g = 0; g < kNP; ++g) {
+      const int s4 = g / C::kDB, db = g % C::kDB;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vr[g % kR], pf[qb][s4], o[qb][db], 0, 0, 0);
+      if (g + kR < kNP) vr[g % kR] = vfrag(v_read, g + kR);
+#pragma unroll
+      for (int p = g * kPairs / kNP; p < (g + 1) * kPairs / kNP; ++p)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          lsum[qb][p >> 2] = __builtin_amdgcn_fdot2(hv[qb][p], ones, lsum[qb][p >> 2], false);
+          asm volatile("" : "+v"(lsum[qb][p >> 2]));  // keeps the sum in this group
+        }
+      __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) l_run[qb] += (lsum[qb][0] + lsum[qb][1]) + (lsum[qb][2] + lsum[qb][3]);
   };
 
   // direct loads issued per iteration by one wave
   constexpr int kPerIter = C::kKDma + C::kVDma;
 
-  // Stage tiles 0..2 (V) and 0..3 (K) and form the scores of tile 0.
+  // Stage tiles 0..1 (V) and 0..3 (K) and form the scores of tile 0.
   f32x16 s_a[QB][2], s_b[QB][2];
   auto prologue = [&]() {
     dma_k(0, k_st0);
@@ -297,7 +365,6 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
     dma_k(1, k_st1);
     dma_v(1, v_st1);
     dma_k(2, k_st2);
-    dma_v(2, v_st2);
     dma_k(3, k_st3);
     wait_vm<0>();
     barrier_only();
@@ -307,29 +374,41 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
     barrier_only();
   };
 
-  // One software-pipelined pass over all key tiles. In iteration t each wave
-  // forms the scores of tile t+1 (MFMA) while it turns the held scores of tile t
-  // into weights (VALU): the two are independent and sit in one branch-free
-  // region, so the matrix and vector units work at the same time. Then
-  // O += V^T(t) P^T(t). Iteration t reads K stage (t+1) % 4 and V stage t % 4 and
-  // issues the direct loads of K(t+4) and V(t+3) into stages t % 4 and
-  // (t+3) % 4, which nobody reads in it; a load thus has three iterations to
-  // land. Staging indices past the last tile re-stage the last tile, and the last
-  // iteration also forms scores it does not use, so the control flow of every
-  // iteration is the same.
+  // One software-pipelined pass over all key tiles. Iteration t issues the
+  // direct loads of V(t+2) and K(t+4), forms the scores of tile t+1 while it
+  // turns the held scores of tile t into weights, then adds V^T(t) P^T(t).
+  //
+  // Waves w and w + WAVES/2 share a SIMD. The lower half passes the iteration's
+  // barrier after the products, the upper half between the two phases, so while
+  // one wave of a SIMD forms scores and weights (matrix and vector work) the
+  // other runs its products (matrix work only): between two barriers the lower
+  // half does S(t+1), W(t), P(t) and the upper half P(t-1), S(t+1), W(t).
+  // Every wave passes one barrier per iteration.
+  //
+  // Stages: K(t) in k_st[t % 4], V(t) in v_st[t % 4]. Between two barriers the
+  // waves read K(t+1), V(t) and V(t-1) and fill K(t+4) and V(t+2), which go to
+  // stages nobody reads then; the barrier closing the interval guarantees V(t+1)
+  // and K(t+2) (issued one and two intervals earlier), so only the newer loads
+  // stay in flight. Staging indices past the last tile re-stage the last tile,
+  // and the last iteration also forms scores it does not use, so the control
+  // flow of every iteration is the same.
+  const bool upper = wave_u >= C::kWaves / 2;
+  auto sync = [&]() {
+    wait_vm<C::kKDma + kPerIter>();
+    barrier_only();
+  };
   auto step = [&](int t, char* k_read, char* k_fill, char* v_read, char* v_fill, f32x16 (&s_cur)[QB][2],
                   f32x16 (&s_next)[QB][2], const float (&mref)[QB]) {
+    dma_v(t + 2, v_fill);
     dma_k(t + 4, k_fill);
-    dma_v(t + 3, v_fill);
+    f16x8 vr[kR];
     f16x8 pf[QB][4];
-    scores(k_read, s_next);
-    weights(s_cur, mref, pf);
-    products(v_read, pf);
+    f16x2 hv[QB][kPairs];
+    score_phase(k_read, v_read, s_cur, s_next, mref, vr, pf, hv);
+    if (upper) sync();
+    product_phase(v_read, vr, pf, hv);
     mask_tail(t + 1, s_next);
-    // the loads of iteration t-2 (needed in iteration t+1) have landed; those of
-    // iterations t-1 and t stay in flight
-    wait_vm<2 * kPerIter>();
-    barrier_only();
+    if (!upper) sync();
   };
   auto main_pass = [&](const float (&mref)[QB]) {
 #pragma unroll
@@ -339,10 +418,10 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
       for (int db = 0; db < C::kDB; ++db) o[qb][db] = f32x16{};
     }
     for (int t = 0; t < ntiles; t += 4) {
-      step(t, k_st1, k_st0, v_st0, v_st3, s_a, s_b, mref);
-      if (t + 1 < ntiles) step(t + 1, k_st2, k_st1, v_st1, v_st0, s_b, s_a, mref);
-      if (t + 2 < ntiles) step(t + 2, k_st3, k_st2, v_st2, v_st1, s_a, s_b, mref);
-      if (t + 3 < ntiles) step(t + 3, k_st0, k_st3, v_st3, v_st2, s_b, s_a, mref);
+      step(t, k_st1, k_st0, v_st0, v_st2, s_a, s_b, mref);
+      if (t + 1 < ntiles) step(t + 1, k_st2, k_st1, v_st1, v_st3, s_b, s_a, mref);
+      if (t + 2 < ntiles) step(t + 2, k_st3, k_st2, v_st2, v_st0, s_a, s_b, mref);
+      if (t + 3 < ntiles) step(t + 3, k_st0, k_st3, v_st3, v_st1, s_b, s_a, mref);
     }
     // drain the direct loads still in flight before the stages are reused
     wait_vm<0>();
