@@ -443,6 +443,12 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   if (__any(bad) && lane == 0) wg_retry = 1;
   __syncthreads();
   if (wg_retry) {
+    // recompute the staging addresses here instead of keeping the prologue's
+    // across the main pass (which would cost registers or scratch there)
+#pragma unroll
+    for (int i = 0; i < C::kKDma; ++i) asm volatile("" : "+v"(kdma_row[i]), "+v"(kdma_off[i]));
+#pragma unroll
+    for (int i = 0; i < C::kVDma; ++i) asm volatile("" : "+v"(vdma_off[i]));
     float mx[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) mx[qb] = -__builtin_inff();
