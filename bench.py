@@ -7,6 +7,10 @@ before timing. One step = the whole hot path through the C ABI: vdit_attn_prepar
 (v -> float16 V^T) then vdit_attn_attend (the attention kernel).
 
 Prints one JSON line. ``value`` = 4 * N * N * d * H / step time (TFLOP/s).
+``kernels`` adds, outside the timed steps, pack/unpack bandwidth and two batched
+calls (two sequences per call, as under classifier-free guidance): the same
+self-attention with B = 2, and text cross-attention over all 40 heads with key
+lengths 512 and 226.
 ``roofline`` prices the attention kernel alone against the MI355X dense
 bf16/fp16 MFMA peak, with its duration from HIP events on the launch stream.
 ``cpu_baseline`` times the float64 oracle on a bounded sample of query rows.
@@ -154,6 +158,40 @@ def main() -> int:
         pack[f"unpack_GBps_n{n}"] = round(nbytes / (e1.elapsed_time(e2) / reps * 1e-3) / 1e9, 1)
         assert torch.equal(y.view(torch.int16), x.view(torch.int16))
 
+    # batch axis: two sequences per call, as for the positive and negative conditioning
+    # of classifier-free guidance. Self-attention at the workload's shape, and text
+    # cross-attention (all 40 heads, 512 text tokens, key lengths 512 and 226).
+    batched = {}
+
+    def time_calls(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    bq, bk, bv = torch.stack((qd, kd)), torch.stack((kd, vdd)), torch.stack((vdd, qd))
+    ab = vd.Attention(N_TOK, N_TOK, HEADS_TOTAL, D, head_begin=HEAD_BEGIN, head_count=HEAD_COUNT, batch=2)
+    wsb = ab.new_workspace(dev)
+    ob = torch.empty(ab.out_shape, dtype=torch.bfloat16, device=dev)
+    ms = time_calls(lambda: ab.forward(bq, bk, bv, out=ob, workspace=wsb), 3)
+    batched["batch2_self_ms"] = round(ms, 3)
+    batched["batch2_self_TFLOPs"] = round(2 * flops / (ms * 1e-3) / 1e12, 1)
+    del bk, bv, wsb, ob, ab
+    lens = (512, 226)
+    xk, xv = torch.stack((kd[:512], vdd[:512])), torch.stack((vdd[:512], qd[:512]))
+    ax = vd.Attention(N_TOK, 512, HEADS_TOTAL, D, use_key_mask=True, batch=2)
+    wsx = ax.new_workspace(dev)
+    ox = torch.empty(ax.out_shape, dtype=torch.bfloat16, device=dev)
+    ms = time_calls(lambda: ax.forward(bq, xk, xv, key_lens=lens, out=ox, workspace=wsx), 5)
+    batched["batch2_cross_ms"] = round(ms, 3)
+    batched["batch2_cross_TFLOPs"] = round(4.0 * N_TOK * sum(lens) * D * HEADS_TOTAL / (ms * 1e-3) / 1e12, 1)
+    del bq, xk, xv, wsx, ox, ax
+
     result = {
         "metric": "attention TFLOP/s + % bf16 MFMA peak at N=75600,H=10,d=128 (1 GPU)",
         "value": round(value, 2),
@@ -186,6 +224,7 @@ def main() -> int:
             "prepare_ms": round(prep_ms, 4),
             "prepare_GBps": round((2 * N_TOK * HEAD_COUNT * D * 2) / (prep_ms * 1e-3) / 1e9, 1),
             **pack,
+            **batched,
         },
     }
     if args.cpu_rows > 0:

@@ -31,10 +31,18 @@
  * multiply-add) and the result is rounded to bfloat16 before the products.
  *
  * Numerics: q.k products in bfloat16 with float32 accumulation; softmax in
- * float32 with a running maximum and sum (online softmax); the weights are
- * rounded to float16 and v is converted once to float16 for the weighted sum
- * (float32 accumulation); the output is rounded to bfloat16 (nearest even).
- * v values must lie within the float16 range (|v| <= 65504).
+ * float32, taken relative to a fixed per-row reference (the maximum over the
+ * first 64 keys; the workgroup recomputes its rows with the exact maximum if a
+ * weight would leave the float16 range); the weights are rounded to float16 and
+ * v is converted once to float16 for the weighted sum (float32 accumulation);
+ * the output is rounded to bfloat16 (nearest even). v values must lie within the
+ * float16 range (|v| <= 65504).
+ * Batch. One call may carry B independent sequences of the same shape, e.g.
+ * the positive and negative conditioning of classifier-free guidance (ComfyUI
+ * issue "MultiGPU Work Units": diffusion models usually run two conditionings,
+ * positive and negative; the fal.ai page, section "Defining the request
+ * schema", exposes the guidance scales). Every tensor then gains a leading [B]
+ * dimension and each entry is computed exactly as a call with B = 1 would.
  *
  * Conventions for every entry point:
  *   - all tensors live in device memory owned by the caller; the library
@@ -90,6 +98,10 @@ typedef enum {
  *   grid_t/h/w      latent grid, grid_t * grid_h * grid_w == nq (used iff use_rope)
  *   rope_dim_t/h/w  band widths, each even and > 0, summing to d (used iff use_rope)
  *   rope_base       base of the frequencies, > 0 and finite (used iff use_rope)
+ *   batch           B, sequences per call (0 is read as 1; at most 64, and B * head_count
+ *                   at most 65535, else UNSUPPORTED). Shapes below then read
+ *                   q [B, nq, Ht, d], k and v [B, nk, Ht, d], packed [B, n, 3, Ht, d],
+ *                   out [B, nq, head_count, d].
  */
 typedef struct {
   int32_t nq;
@@ -105,6 +117,7 @@ typedef struct {
   int32_t grid_t, grid_h, grid_w;
   int32_t rope_dim_t, rope_dim_h, rope_dim_w;
   double rope_base;
+  int32_t batch;
 } vdit_attn_desc_t;
 
 /*
@@ -137,9 +150,9 @@ vdit_status_t vdit_attn_destroy(vdit_attn_t h);
 
 /*
  * Bytes of caller-provided device workspace that prepare/attend/fwd need for the
- * largest key length of this plan: v transposed to float16 per head
- * ([head_count][ceil(nk/64)*64][d], 2 bytes) and, with use_rope, the rotated keys
- * per head (same shape, bfloat16). Host only.
+ * largest key length of this plan: v transposed to float16 per entry and head
+ * ([B][head_count][ceil(nk/64)*64][d], 2 bytes) and, with use_rope, the rotated keys
+ * (same shape, bfloat16). Host only.
  */
 vdit_status_t vdit_attn_workspace_bytes(vdit_attn_t h, size_t* bytes);
 
@@ -149,6 +162,7 @@ vdit_status_t vdit_attn_workspace_bytes(vdit_attn_t h, size_t* bytes);
  *              N3HD: q is the packed [n, 3, Ht, d] tensor; k and v must be NULL.
  *   key_len    used iff use_key_mask: 1 <= key_len <= nk (keys j >= key_len are
  *              excluded; their k and v contents are never read); otherwise ignored.
+ *              With B > 1 it applies to every entry (see the _lens calls below).
  *   out        bfloat16 [nq, head_count, d], contiguous; must not overlap the inputs
  *              or the workspace.
  *   workspace  >= vdit_attn_workspace_bytes() bytes of device memory; its contents
@@ -177,6 +191,25 @@ vdit_status_t vdit_attn_prepare(vdit_attn_t h, const void* q, const void* k, con
 vdit_status_t vdit_attn_attend(vdit_attn_t h, const void* q, const void* k, const void* v,
                                int32_t key_len, void* out, void* workspace, size_t workspace_bytes,
                                void* hip_stream);
+
+/*
+ * fwd, prepare and attend with one key length per batch entry, for batches whose
+ * sequences mask different numbers of keys (e.g. positive and negative prompts of
+ * different text lengths under classifier-free guidance). key_lens: host array of
+ * B int32 values, read during the call only; used iff use_key_mask, then each must
+ * satisfy 1 <= key_lens[b] <= nk and the pointer must not be NULL (INVALID_ARG
+ * otherwise); NULL is accepted without use_key_mask. prepare and attend must see
+ * the same lengths. Other arguments as for fwd / prepare / attend.
+ */
+vdit_status_t vdit_attn_fwd_lens(vdit_attn_t h, const void* q, const void* k, const void* v,
+                                 const int32_t* key_lens, void* out, void* workspace,
+                                 size_t workspace_bytes, void* hip_stream);
+vdit_status_t vdit_attn_prepare_lens(vdit_attn_t h, const void* q, const void* k, const void* v,
+                                     const int32_t* key_lens, void* workspace, size_t workspace_bytes,
+                                     void* hip_stream);
+vdit_status_t vdit_attn_attend_lens(vdit_attn_t h, const void* q, const void* k, const void* v,
+                                    const int32_t* key_lens, void* out, void* workspace,
+                                    size_t workspace_bytes, void* hip_stream);
 
 /*
  * Layout change for the Ulysses exchange (fal.ai page, section "Splitting one

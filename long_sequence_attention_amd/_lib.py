@@ -22,7 +22,7 @@ class Desc(ctypes.Structure):
         ("head_count", ctypes.c_int32), ("scale", ctypes.c_float), ("use_key_mask", ctypes.c_int32),
         ("use_rope", ctypes.c_int32), ("grid_t", ctypes.c_int32), ("grid_h", ctypes.c_int32),
         ("grid_w", ctypes.c_int32), ("rope_dim_t", ctypes.c_int32), ("rope_dim_h", ctypes.c_int32),
-        ("rope_dim_w", ctypes.c_int32), ("rope_base", ctypes.c_double),
+        ("rope_dim_w", ctypes.c_int32), ("rope_base", ctypes.c_double), ("batch", ctypes.c_int32),
     ]
 
 
@@ -40,6 +40,9 @@ SIGNATURES = {
     "vdit_attn_fwd": (_ST, [_P, _P, _P, _P, _I, _P, _P, _S, _P]),
     "vdit_attn_prepare": (_ST, [_P, _P, _P, _P, _I, _P, _S, _P]),
     "vdit_attn_attend": (_ST, [_P, _P, _P, _P, _I, _P, _P, _S, _P]),
+    "vdit_attn_fwd_lens": (_ST, [_P, _P, _P, _P, ctypes.POINTER(_I), _P, _P, _S, _P]),
+    "vdit_attn_prepare_lens": (_ST, [_P, _P, _P, _P, ctypes.POINTER(_I), _P, _S, _P]),
+    "vdit_attn_attend_lens": (_ST, [_P, _P, _P, _P, ctypes.POINTER(_I), _P, _P, _S, _P]),
     "vdit_pack_heads": (_ST, [_P, _P, _I, _I, _I, _I, _P]),
     "vdit_unpack_heads": (_ST, [_P, _P, _I, _I, _I, _I, _P]),
     "vdit_attn_rope_probe": (_ST, [_P, _P, _P]),

@@ -62,8 +62,9 @@ def ulysses_heads(heads_total: int, degree: int, rank: int) -> tuple[int, int]:
 
 def make_desc(nq: int, nk: int, heads_total: int, head_dim: int, *, layout: str = "NHD", head_begin: int = 0,
               head_count: int | None = None, scale: float = 0.0, use_key_mask: bool = False,
-              rope: dict | None = None) -> _lib.Desc:
+              rope: dict | None = None, batch: int = 1) -> _lib.Desc:
     d = _lib.Desc()
+    d.batch = batch
     d.nq, d.nk, d.heads_total, d.head_dim = nq, nk, heads_total, head_dim
     d.layout = {"NHD": _lib.LAYOUT_NHD, "N3HD": _lib.LAYOUT_N3HD}[layout]
     d.head_begin = head_begin
@@ -86,15 +87,21 @@ def create_raw(desc: _lib.Desc) -> tuple[int, int]:
 
 
 class Attention:
-    """One attention plan (vdit_attn_t) and its calls on torch tensors."""
+    """One attention plan (vdit_attn_t) and its calls on torch tensors.
+
+    With ``batch`` = B > 1 every tensor has a leading [B] dimension; the calls take
+    either one ``key_len`` for all entries or ``key_lens`` (B values).
+    """
 
     def __init__(self, nq: int, nk: int, heads_total: int, head_dim: int, *, layout: str = "NHD",
                  head_begin: int = 0, head_count: int | None = None, scale: float = 0.0,
-                 use_key_mask: bool = False, rope: dict | None = None):
+                 use_key_mask: bool = False, rope: dict | None = None, batch: int = 1):
         self._lib = _lib.load()
         self.desc = make_desc(nq, nk, heads_total, head_dim, layout=layout, head_begin=head_begin,
-                              head_count=head_count, scale=scale, use_key_mask=use_key_mask, rope=rope)
+                              head_count=head_count, scale=scale, use_key_mask=use_key_mask, rope=rope,
+                              batch=batch)
         self.layout = layout
+        self.batch = int(batch)
         h = ctypes.c_void_p()
         _check(self._lib.vdit_attn_create(ctypes.byref(self.desc), ctypes.byref(h)), "vdit_attn_create")
         self._h = h
@@ -103,21 +110,33 @@ class Attention:
         self.workspace_bytes = int(n.value)
 
     # -- shapes
+    def _lead(self):
+        return (self.batch,) if self.batch > 1 else ()
+
     @property
     def out_shape(self):
         d = self.desc
-        return (d.nq, d.head_count, d.head_dim)
+        return self._lead() + (d.nq, d.head_count, d.head_dim)
 
     def _check_inputs(self, q, k, v):
         d = self.desc
+        b = self._lead()
         if self.layout == "N3HD":
-            _need(q, (d.nq, 3, d.heads_total, d.head_dim), torch.bfloat16, "qkv")
+            _need(q, b + (d.nq, 3, d.heads_total, d.head_dim), torch.bfloat16, "qkv")
             if k is not None or v is not None:
                 raise ValueError("the packed layout takes the [N, 3, H, d] tensor alone")
         else:
-            _need(q, (d.nq, d.heads_total, d.head_dim), torch.bfloat16, "q")
-            _need(k, (d.nk, d.heads_total, d.head_dim), torch.bfloat16, "k")
-            _need(v, (d.nk, d.heads_total, d.head_dim), torch.bfloat16, "v")
+            _need(q, b + (d.nq, d.heads_total, d.head_dim), torch.bfloat16, "q")
+            _need(k, b + (d.nk, d.heads_total, d.head_dim), torch.bfloat16, "k")
+            _need(v, b + (d.nk, d.heads_total, d.head_dim), torch.bfloat16, "v")
+
+    def _lens(self, key_lens):
+        if key_lens is None:
+            return None
+        lens = [int(x) for x in key_lens]
+        if len(lens) != self.batch:
+            raise ValueError(f"key_lens needs {self.batch} values, got {len(lens)}")
+        return (ctypes.c_int32 * len(lens))(*lens)
 
     def new_workspace(self, device) -> torch.Tensor:
         return torch.empty(max(self.workspace_bytes, 16), dtype=torch.uint8, device=device)
@@ -130,36 +149,54 @@ class Attention:
         return workspace
 
     # -- calls
-    def forward(self, q, k=None, v=None, *, key_len: int = 0, out=None, workspace=None, stream=None):
+    def forward(self, q, k=None, v=None, *, key_len: int = 0, key_lens=None, out=None, workspace=None,
+                stream=None):
         self._check_inputs(q, k, v)
         if out is None:
             out = torch.empty(self.out_shape, dtype=torch.bfloat16, device=q.device)
         _need(out, self.out_shape, torch.bfloat16, "out")
         ws = self._ws(workspace, q.device)
-        _check(self._lib.vdit_attn_fwd(self._h, _ptr(q), _ptr(k), _ptr(v), int(key_len), _ptr(out), _ptr(ws),
-                                       ws.numel() * ws.element_size(), _stream_ptr(q, stream)), "vdit_attn_fwd")
+        nbytes, sp = ws.numel() * ws.element_size(), _stream_ptr(q, stream)
+        lens = self._lens(key_lens)
+        if lens is None:
+            _check(self._lib.vdit_attn_fwd(self._h, _ptr(q), _ptr(k), _ptr(v), int(key_len), _ptr(out), _ptr(ws),
+                                           nbytes, sp), "vdit_attn_fwd")
+        else:
+            _check(self._lib.vdit_attn_fwd_lens(self._h, _ptr(q), _ptr(k), _ptr(v), lens, _ptr(out), _ptr(ws),
+                                                nbytes, sp), "vdit_attn_fwd_lens")
         return out
 
     __call__ = forward
 
-    def prepare(self, q, k=None, v=None, *, key_len: int = 0, workspace=None, stream=None):
+    def prepare(self, q, k=None, v=None, *, key_len: int = 0, key_lens=None, workspace=None, stream=None):
         self._check_inputs(q, k, v)
         ws = self._ws(workspace, q.device)
-        _check(self._lib.vdit_attn_prepare(self._h, _ptr(q), _ptr(k), _ptr(v), int(key_len), _ptr(ws),
-                                           ws.numel() * ws.element_size(), _stream_ptr(q, stream)),
-               "vdit_attn_prepare")
+        nbytes, sp = ws.numel() * ws.element_size(), _stream_ptr(q, stream)
+        lens = self._lens(key_lens)
+        if lens is None:
+            _check(self._lib.vdit_attn_prepare(self._h, _ptr(q), _ptr(k), _ptr(v), int(key_len), _ptr(ws), nbytes,
+                                               sp), "vdit_attn_prepare")
+        else:
+            _check(self._lib.vdit_attn_prepare_lens(self._h, _ptr(q), _ptr(k), _ptr(v), lens, _ptr(ws), nbytes,
+                                                    sp), "vdit_attn_prepare_lens")
         return ws
 
-    def attend(self, q, k=None, v=None, *, key_len: int = 0, out=None, workspace=None, stream=None):
+    def attend(self, q, k=None, v=None, *, key_len: int = 0, key_lens=None, out=None, workspace=None,
+               stream=None):
         self._check_inputs(q, k, v)
         if workspace is None:
             raise ValueError("attend needs the workspace filled by prepare")
         if out is None:
             out = torch.empty(self.out_shape, dtype=torch.bfloat16, device=q.device)
         _need(out, self.out_shape, torch.bfloat16, "out")
-        _check(self._lib.vdit_attn_attend(self._h, _ptr(q), _ptr(k), _ptr(v), int(key_len), _ptr(out),
-                                          _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                          _stream_ptr(q, stream)), "vdit_attn_attend")
+        nbytes, sp = workspace.numel() * workspace.element_size(), _stream_ptr(q, stream)
+        lens = self._lens(key_lens)
+        if lens is None:
+            _check(self._lib.vdit_attn_attend(self._h, _ptr(q), _ptr(k), _ptr(v), int(key_len), _ptr(out),
+                                              _ptr(workspace), nbytes, sp), "vdit_attn_attend")
+        else:
+            _check(self._lib.vdit_attn_attend_lens(self._h, _ptr(q), _ptr(k), _ptr(v), lens, _ptr(out),
+                                                   _ptr(workspace), nbytes, sp), "vdit_attn_attend_lens")
         return out
 
     def rope_probe(self, device, stream=None) -> torch.Tensor:

@@ -11,7 +11,7 @@
 #include "vdit_attn.h"
 
 struct vdit_attn {
-  vdit_attn_desc_t desc;
+  vdit_attn_desc_t desc;  // batch normalised to >= 1
   float scale;
   float c;             // scale * log2(e)
   int device;
@@ -50,20 +50,22 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 vdit_status_t validate_desc(const vdit_attn_desc_t& d) {
+  if (d.batch < 0) return VDIT_ERR_INVALID_ARG;
   if (d.head_dim != 64 && d.head_dim != 128) return VDIT_ERR_UNSUPPORTED;
   if (d.nq < 1 || d.nk < 1 || d.heads_total < 1) return VDIT_ERR_INVALID_ARG;
   if (d.layout != VDIT_LAYOUT_NHD && d.layout != VDIT_LAYOUT_N3HD) return VDIT_ERR_INVALID_ARG;
   if (d.layout == VDIT_LAYOUT_N3HD && d.nq != d.nk) return VDIT_ERR_INVALID_ARG;
   if (d.head_begin < 0 || d.head_count < 1 || (int64_t)d.head_begin + d.head_count > d.heads_total)
     return VDIT_ERR_INVALID_ARG;
-  if (d.head_count > 65535) return VDIT_ERR_UNSUPPORTED;
+  const int64_t batch = d.batch > 0 ? d.batch : 1;
+  if (batch > vdit::kMaxBatch || (int64_t)d.head_count * batch > 65535) return VDIT_ERR_UNSUPPORTED;
   if (std::isnan(d.scale) || std::isinf(d.scale)) return VDIT_ERR_INVALID_ARG;
   if (d.use_key_mask != 0 && d.use_key_mask != 1) return VDIT_ERR_INVALID_ARG;
   if (d.use_rope != 0 && d.use_rope != 1) return VDIT_ERR_INVALID_ARG;
   // element offsets are 64-bit in the kernels; keep every tensor below 2^60 elements
   const int64_t row = (int64_t)d.heads_total * d.head_dim * (d.layout == VDIT_LAYOUT_N3HD ? 3 : 1);
   const int64_t nmax = d.nq > d.nk ? d.nq : d.nk;
-  if (row > (int64_t(1) << 40) || nmax * row > (int64_t(1) << 60)) return VDIT_ERR_INVALID_ARG;
+  if (row > (int64_t(1) << 40) || batch * nmax * row > (int64_t(1) << 60)) return VDIT_ERR_INVALID_ARG;
   if (d.use_rope) {
     if (d.nq != d.nk) return VDIT_ERR_INVALID_ARG;
     if (d.grid_t < 1 || d.grid_h < 1 || d.grid_w < 1) return VDIT_ERR_INVALID_ARG;
@@ -109,9 +111,10 @@ void build_rope_table(const vdit_attn_desc_t& d, std::vector<float2>& tab, vdit:
 }
 
 struct Inputs {
-  const __bf16 *q, *k, *v;  // pointing at head_begin, token 0
+  const __bf16 *q, *k, *v;  // pointing at head_begin, token 0, batch entry 0
   int64_t q_row, kv_row;
-  size_t q_bytes, k_bytes, v_bytes;  // extents for the overlap checks
+  int64_t q_batch, kv_batch;  // elements between batch entries
+  size_t q_bytes, k_bytes, v_bytes;  // extents (all entries) for the overlap checks
   const void *q_base, *k_base, *v_base;
 };
 
@@ -127,7 +130,8 @@ vdit_status_t resolve_inputs(const vdit_attn& h, const void* q, const void* k, c
     in.k = base + hd;
     in.v = base + 2 * hd;
     in.q_row = in.kv_row = 3 * hd;
-    in.q_bytes = (size_t)d.nq * 3 * hd * 2;
+    in.q_batch = in.kv_batch = (int64_t)d.nq * 3 * hd;
+    in.q_bytes = (size_t)d.batch * d.nq * 3 * hd * 2;
     in.k_bytes = in.v_bytes = 0;
     in.q_base = q;
     in.k_base = in.v_base = nullptr;
@@ -139,8 +143,10 @@ vdit_status_t resolve_inputs(const vdit_attn& h, const void* q, const void* k, c
     in.k = static_cast<const __bf16*>(k) + off;
     in.v = static_cast<const __bf16*>(v) + off;
     in.q_row = in.kv_row = hd;
-    in.q_bytes = (size_t)d.nq * hd * 2;
-    in.k_bytes = in.v_bytes = (size_t)d.nk * hd * 2;
+    in.q_batch = (int64_t)d.nq * hd;
+    in.kv_batch = (int64_t)d.nk * hd;
+    in.q_bytes = (size_t)d.batch * d.nq * hd * 2;
+    in.k_bytes = in.v_bytes = (size_t)d.batch * d.nk * hd * 2;
     in.q_base = q;
     in.k_base = k;
     in.v_base = v;
@@ -148,14 +154,32 @@ vdit_status_t resolve_inputs(const vdit_attn& h, const void* q, const void* k, c
   return VDIT_OK;
 }
 
-vdit_status_t check_call(const vdit_attn& h, int32_t key_len, void* workspace, size_t ws_bytes, int32_t& kv_len) {
+// Valid key count of every batch entry: from key_lens (B values) when given, else
+// key_len for all; both are used only with the key mask.
+struct KeyLens {
+  int32_t len[vdit::kMaxBatch];
+  int32_t max;
+};
+
+vdit_status_t resolve_lens(const vdit_attn& h, bool per_entry, int32_t key_len, const int32_t* key_lens,
+                           KeyLens& kl) {
   const vdit_attn_desc_t& d = h.desc;
-  if (d.use_key_mask) {
-    if (key_len < 1 || key_len > d.nk) return VDIT_ERR_INVALID_ARG;
-    kv_len = key_len;
-  } else {
-    kv_len = d.nk;
+  kl.max = 0;
+  for (int32_t b = 0; b < vdit::kMaxBatch; ++b) kl.len[b] = 0;
+  if (d.use_key_mask && per_entry && !key_lens) return VDIT_ERR_INVALID_ARG;
+  for (int32_t b = 0; b < d.batch; ++b) {
+    int32_t L = d.nk;
+    if (d.use_key_mask) {
+      L = per_entry ? key_lens[b] : key_len;
+      if (L < 1 || L > d.nk) return VDIT_ERR_INVALID_ARG;
+    }
+    kl.len[b] = L;
+    if (L > kl.max) kl.max = L;
   }
+  return VDIT_OK;
+}
+
+vdit_status_t check_call(const vdit_attn& h, void* workspace, size_t ws_bytes) {
   if (!workspace || ws_bytes < h.ws_total) return VDIT_ERR_WORKSPACE;
   if (!aligned16(workspace)) return VDIT_ERR_ALIGNMENT;
   int dev = -1;
@@ -163,48 +187,57 @@ vdit_status_t check_call(const vdit_attn& h, int32_t key_len, void* workspace, s
   return VDIT_OK;
 }
 
-vdit_status_t do_prepare(const vdit_attn& h, const Inputs& in, int32_t kv_len, void* ws, hipStream_t s) {
+vdit_status_t do_prepare(const vdit_attn& h, const Inputs& in, const KeyLens& kl, void* ws, hipStream_t s) {
   const vdit_attn_desc_t& d = h.desc;
   vdit::PrepArgs a{};
   a.k = in.k;
   a.v = in.v;
   a.kv_row = in.kv_row;
   a.kv_head = d.head_dim;
+  a.kv_batch = in.kv_batch;
   a.vt = reinterpret_cast<_Float16*>(static_cast<char*>(ws) + h.ws_vt_off);
   a.vt_head = h.nk_pad * d.head_dim;
   a.kr = d.use_rope ? reinterpret_cast<__bf16*>(static_cast<char*>(ws) + h.ws_kr_off) : nullptr;
   a.kr_head = h.nk_pad * d.head_dim;
-  a.kv_len = kv_len;
-  a.n_ktiles = (kv_len + vdit::kBlockN - 1) / vdit::kBlockN;
+  a.n_ktiles = (kl.max + vdit::kBlockN - 1) / vdit::kBlockN;
   a.hc = d.head_count;
+  a.batch = d.batch;
   a.rope = h.geom;
+  for (int32_t b = 0; b < vdit::kMaxBatch; ++b) a.kv_len[b] = kl.len[b];
   if (vdit::launch_prepare(a, d.head_dim, d.use_rope != 0, s) != hipSuccess) return VDIT_ERR_DEVICE;
   return VDIT_OK;
 }
 
-vdit_status_t do_attend(const vdit_attn& h, const Inputs& in, int32_t kv_len, void* out, void* ws, hipStream_t s) {
+vdit_status_t do_attend(const vdit_attn& h, const Inputs& in, const KeyLens& kl, void* out, void* ws,
+                        hipStream_t s) {
   const vdit_attn_desc_t& d = h.desc;
   vdit::AttnArgs a{};
   a.q = in.q;
   a.q_row = in.q_row;
   a.q_head = d.head_dim;
+  a.q_batch = in.q_batch;
   if (d.use_rope) {
     a.k = reinterpret_cast<const __bf16*>(static_cast<const char*>(ws) + h.ws_kr_off);
     a.k_row = d.head_dim;
     a.k_head = h.nk_pad * d.head_dim;
+    a.k_batch = a.k_head * d.head_count;
   } else {
     a.k = in.k;
     a.k_row = in.kv_row;
     a.k_head = d.head_dim;
+    a.k_batch = in.kv_batch;
   }
   a.vt = reinterpret_cast<const _Float16*>(static_cast<const char*>(ws) + h.ws_vt_off);
   a.vt_head = h.nk_pad * d.head_dim;
+  a.vt_batch = a.vt_head * d.head_count;
   a.out = static_cast<__bf16*>(out);
+  a.out_batch = (int64_t)d.nq * d.head_count * d.head_dim;
   a.nq = d.nq;
-  a.kv_len = kv_len;
   a.hc = d.head_count;
+  a.batch = d.batch;
   a.c = h.c;
   a.rope = h.geom;
+  for (int32_t b = 0; b < vdit::kMaxBatch; ++b) a.kv_len[b] = kl.len[b];
   if (vdit::launch_attn_fwd(a, d.head_dim, d.use_rope != 0, s) != hipSuccess) return VDIT_ERR_DEVICE;
   return VDIT_OK;
 }
@@ -212,7 +245,7 @@ vdit_status_t do_attend(const vdit_attn& h, const Inputs& in, int32_t kv_len, vo
 vdit_status_t check_out(const vdit_attn& h, const Inputs& in, void* out, const void* ws) {
   if (!out) return VDIT_ERR_INVALID_ARG;
   if (!aligned16(out)) return VDIT_ERR_ALIGNMENT;
-  const size_t ob = (size_t)h.desc.nq * h.desc.head_count * h.desc.head_dim * 2;
+  const size_t ob = (size_t)h.desc.batch * h.desc.nq * h.desc.head_count * h.desc.head_dim * 2;
   if (overlaps(out, ob, in.q_base, in.q_bytes) || overlaps(out, ob, in.k_base, in.k_bytes) ||
       overlaps(out, ob, in.v_base, in.v_bytes) || overlaps(out, ob, ws, h.ws_total))
     return VDIT_ERR_INVALID_ARG;
@@ -251,6 +284,7 @@ vdit_status_t vdit_attn_create(const vdit_attn_desc_t* desc, vdit_attn_t* out) {
   if (!hp) return VDIT_ERR_OUT_OF_MEMORY;
   vdit_attn& h = *hp;
   h.desc = *desc;
+  if (h.desc.batch < 1) h.desc.batch = 1;
   const vdit_attn_desc_t& d = h.desc;
   const double scale = d.scale > 0.0f ? (double)d.scale : 1.0 / std::sqrt((double)d.head_dim);
   h.scale = (float)scale;
@@ -258,9 +292,9 @@ vdit_status_t vdit_attn_create(const vdit_attn_desc_t* desc, vdit_attn_t* out) {
   h.nk_pad = ((int64_t)d.nk + vdit::kBlockN - 1) / vdit::kBlockN * vdit::kBlockN;
   const size_t per_head = (size_t)h.nk_pad * d.head_dim * 2;
   h.ws_vt_off = 0;
-  h.ws_vt_bytes = per_head * d.head_count;
+  h.ws_vt_bytes = per_head * d.head_count * d.batch;
   h.ws_kr_off = align_up(h.ws_vt_bytes, 256);
-  h.ws_kr_bytes = d.use_rope ? per_head * d.head_count : 0;
+  h.ws_kr_bytes = d.use_rope ? per_head * d.head_count * d.batch : 0;
   h.ws_total = d.use_rope ? h.ws_kr_off + h.ws_kr_bytes : h.ws_vt_bytes;
   h.rope_tab = nullptr;
   h.geom = vdit::RopeGeom{};
@@ -310,44 +344,64 @@ vdit_status_t vdit_attn_workspace_bytes(vdit_attn_t h, size_t* bytes) {
   return VDIT_OK;
 }
 
-vdit_status_t vdit_attn_prepare(vdit_attn_t h, const void* q, const void* k, const void* v, int32_t key_len,
-                                void* workspace, size_t workspace_bytes, void* hip_stream) {
+}  // extern "C"
+
+namespace {
+
+enum class Stage { kPrepare, kAttend, kBoth };
+
+vdit_status_t run(vdit_attn_t h, const void* q, const void* k, const void* v, bool per_entry, int32_t key_len,
+                  const int32_t* key_lens, void* out, void* workspace, size_t workspace_bytes, void* hip_stream,
+                  Stage stage) {
   if (!is_live(h)) return VDIT_ERR_INVALID_ARG;
   Inputs in{};
   vdit_status_t st = resolve_inputs(*h, q, k, v, in);
   if (st != VDIT_OK) return st;
-  int32_t kv_len = 0;
-  if ((st = check_call(*h, key_len, workspace, workspace_bytes, kv_len)) != VDIT_OK) return st;
+  if (stage != Stage::kPrepare && (st = check_out(*h, in, out, workspace)) != VDIT_OK) return st;
+  KeyLens kl;
+  if ((st = resolve_lens(*h, per_entry, key_len, key_lens, kl)) != VDIT_OK) return st;
+  if ((st = check_call(*h, workspace, workspace_bytes)) != VDIT_OK) return st;
   if ((st = check_ws_inputs(*h, in, workspace)) != VDIT_OK) return st;
-  return do_prepare(*h, in, kv_len, workspace, static_cast<hipStream_t>(hip_stream));
+  const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  if (stage != Stage::kAttend && (st = do_prepare(*h, in, kl, workspace, s)) != VDIT_OK) return st;
+  if (stage != Stage::kPrepare) return do_attend(*h, in, kl, out, workspace, s);
+  return VDIT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+vdit_status_t vdit_attn_prepare(vdit_attn_t h, const void* q, const void* k, const void* v, int32_t key_len,
+                                void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return run(h, q, k, v, false, key_len, nullptr, nullptr, workspace, workspace_bytes, hip_stream, Stage::kPrepare);
 }
 
 vdit_status_t vdit_attn_attend(vdit_attn_t h, const void* q, const void* k, const void* v, int32_t key_len,
                                void* out, void* workspace, size_t workspace_bytes, void* hip_stream) {
-  if (!is_live(h)) return VDIT_ERR_INVALID_ARG;
-  Inputs in{};
-  vdit_status_t st = resolve_inputs(*h, q, k, v, in);
-  if (st != VDIT_OK) return st;
-  if ((st = check_out(*h, in, out, workspace)) != VDIT_OK) return st;
-  int32_t kv_len = 0;
-  if ((st = check_call(*h, key_len, workspace, workspace_bytes, kv_len)) != VDIT_OK) return st;
-  if ((st = check_ws_inputs(*h, in, workspace)) != VDIT_OK) return st;
-  return do_attend(*h, in, kv_len, out, workspace, static_cast<hipStream_t>(hip_stream));
+  return run(h, q, k, v, false, key_len, nullptr, out, workspace, workspace_bytes, hip_stream, Stage::kAttend);
 }
 
 vdit_status_t vdit_attn_fwd(vdit_attn_t h, const void* q, const void* k, const void* v, int32_t key_len, void* out,
                             void* workspace, size_t workspace_bytes, void* hip_stream) {
-  if (!is_live(h)) return VDIT_ERR_INVALID_ARG;
-  Inputs in{};
-  vdit_status_t st = resolve_inputs(*h, q, k, v, in);
-  if (st != VDIT_OK) return st;
-  if ((st = check_out(*h, in, out, workspace)) != VDIT_OK) return st;
-  int32_t kv_len = 0;
-  if ((st = check_call(*h, key_len, workspace, workspace_bytes, kv_len)) != VDIT_OK) return st;
-  if ((st = check_ws_inputs(*h, in, workspace)) != VDIT_OK) return st;
-  const hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  if ((st = do_prepare(*h, in, kv_len, workspace, s)) != VDIT_OK) return st;
-  return do_attend(*h, in, kv_len, out, workspace, s);
+  return run(h, q, k, v, false, key_len, nullptr, out, workspace, workspace_bytes, hip_stream, Stage::kBoth);
+}
+
+vdit_status_t vdit_attn_prepare_lens(vdit_attn_t h, const void* q, const void* k, const void* v,
+                                     const int32_t* key_lens, void* workspace, size_t workspace_bytes,
+                                     void* hip_stream) {
+  return run(h, q, k, v, true, 0, key_lens, nullptr, workspace, workspace_bytes, hip_stream, Stage::kPrepare);
+}
+
+vdit_status_t vdit_attn_attend_lens(vdit_attn_t h, const void* q, const void* k, const void* v,
+                                    const int32_t* key_lens, void* out, void* workspace, size_t workspace_bytes,
+                                    void* hip_stream) {
+  return run(h, q, k, v, true, 0, key_lens, out, workspace, workspace_bytes, hip_stream, Stage::kAttend);
+}
+
+vdit_status_t vdit_attn_fwd_lens(vdit_attn_t h, const void* q, const void* k, const void* v, const int32_t* key_lens,
+                                 void* out, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return run(h, q, k, v, true, 0, key_lens, out, workspace, workspace_bytes, hip_stream, Stage::kBoth);
 }
 
 static vdit_status_t pack_common(const void* src, void* dst, int32_t n, int32_t ht, int32_t d, int32_t groups,

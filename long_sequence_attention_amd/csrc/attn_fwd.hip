@@ -110,8 +110,10 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   const int per = nwg >> 3;
   const int rem = nwg & 7;
   const int id = xcd * per + (xcd < rem ? xcd : rem) + (wg >> 3);
-  const int head = id / a.n_qtiles;
-  const int qtile = id - head * a.n_qtiles;
+  const int bh = id / a.n_qtiles;          // batch entry * hc + local head
+  const int qtile = id - bh * a.n_qtiles;
+  const int bat = bh / a.hc;
+  const int head = bh - bat * a.hc;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -128,7 +130,7 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   for (int qb = 0; qb < QB; ++qb) {
     const int qi = q0 + qb * 32 + l32;
     if (qi < a.nq) {
-      const __bf16* qp = a.q + (int64_t)qi * a.q_row + (int64_t)head * a.q_head + 8 * hl;
+      const __bf16* qp = a.q + bat * a.q_batch + (int64_t)qi * a.q_row + (int64_t)head * a.q_head + 8 * hl;
       int t = 0, y = 0, x = 0;
       if constexpr (ROPE) rope_token_pos(a.rope, qi, t, y, x);
 #pragma unroll
@@ -143,11 +145,11 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
     }
   }
 
-  const int kv_len = a.kv_len;
+  const int kv_len = a.kv_len[bat];
   const int ntiles = (kv_len + kBlockN - 1) / kBlockN;
   const float c = a.c;
-  const char* kbytes = reinterpret_cast<const char*>(a.k + (int64_t)head * a.k_head);
-  const char* vbytes = reinterpret_cast<const char*>(a.vt + (int64_t)head * a.vt_head);
+  const char* kbytes = reinterpret_cast<const char*>(a.k + bat * a.k_batch + (int64_t)head * a.k_head);
+  const char* vbytes = reinterpret_cast<const char*>(a.vt + bat * a.vt_batch + (int64_t)head * a.vt_head);
   const int krow_bytes = (int)(a.k_row * 2);
 
   // ---- direct global -> LDS staging. Wave w fills the 1 KB pieces w*n .. w*n+n-1
@@ -476,7 +478,7 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
     const float inv = 1.0f / lt;
     const int qi = q0 + qb * 32 + l32;
     if (qi < a.nq) {
-      __bf16* op = a.out + ((int64_t)qi * a.hc + head) * D + 4 * hl;
+      __bf16* op = a.out + bat * a.out_batch + ((int64_t)qi * a.hc + head) * D + 4 * hl;
 #pragma unroll
       for (int db = 0; db < C::kDB; ++db)
 #pragma unroll
@@ -494,7 +496,7 @@ template <int D, int QB, int WAVES, bool ROPE>
 hipError_t launch_fwd_t(AttnArgs a, hipStream_t s) {
   using C = FwdCfg<D, QB, WAVES>;
   a.n_qtiles = (a.nq + C::kBlockM - 1) / C::kBlockM;
-  const int64_t nwg = (int64_t)a.n_qtiles * a.hc;
+  const int64_t nwg = (int64_t)a.n_qtiles * a.hc * a.batch;
   if (nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL((attn_fwd_kernel<D, QB, WAVES, ROPE>), dim3((unsigned)nwg), dim3(C::kThreads), 0, s, a);
   return hipGetLastError();
@@ -503,6 +505,7 @@ hipError_t launch_fwd_t(AttnArgs a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_attn_fwd(const AttnArgs& a, int head_dim, bool rope_q, hipStream_t s) {
+  if (a.batch <= 0 || a.batch > kMaxBatch || a.hc <= 0) return hipErrorInvalidValue;
   if (head_dim == 128) return rope_q ? launch_fwd_t<128, 1, 8, true>(a, s) : launch_fwd_t<128, 1, 8, false>(a, s);
   if (head_dim == 64) return rope_q ? launch_fwd_t<64, 1, 8, true>(a, s) : launch_fwd_t<64, 1, 8, false>(a, s);
   return hipErrorInvalidValue;

@@ -84,37 +84,48 @@ __device__ __forceinline__ bf16x8 rope_chunk(const RopeGeom& g, bf16x8 v, int32_
 // Launch parameter blocks.
 // ---------------------------------------------------------------------------
 
+// Sequences per call (batch entries) whose key lengths travel in the launch arguments.
+constexpr int kMaxBatch = 64;
+
+// Element offsets of batch entry b are b * (the *_batch stride) on top of those below.
 struct AttnArgs {
-  const __bf16* q;       // q of head `head_begin`, token 0
+  const __bf16* q;       // q of head `head_begin`, token 0, entry 0
   int64_t q_row;         // elements between consecutive tokens of q
+  int64_t q_batch;       // elements between batch entries of q
   const __bf16* k;       // k of local head 0, key 0 (input or rotated workspace copy)
   int64_t k_row;         // elements between consecutive keys
   int64_t k_head;        // elements between consecutive local heads of k
+  int64_t k_batch;
   const _Float16* vt;    // transposed float16 v in the workspace, local head 0
   int64_t vt_head;       // elements between heads of vt
-  __bf16* out;           // [nq, hc, d]
+  int64_t vt_batch;
+  __bf16* out;           // [B, nq, hc, d]
+  int64_t out_batch;
   int32_t nq;
-  int32_t kv_len;        // valid keys
   int32_t hc;            // heads in the share
   int32_t n_qtiles;      // query tiles per head
+  int32_t batch;         // B
   float c;               // scale * log2(e)
   int32_t q_head;        // elements between consecutive heads of q (= d)
   RopeGeom rope;
+  int32_t kv_len[kMaxBatch];  // valid keys of each entry
 };
 
 struct PrepArgs {
-  const __bf16* k;       // k of head `head_begin`, key 0
-  const __bf16* v;       // v of head `head_begin`, key 0
+  const __bf16* k;       // k of head `head_begin`, key 0, entry 0
+  const __bf16* v;       // v of head `head_begin`, key 0, entry 0
   int64_t kv_row;        // elements between consecutive keys
   int64_t kv_head;       // elements between consecutive heads (= d)
+  int64_t kv_batch;      // elements between batch entries of k and v
   _Float16* vt;          // workspace vt, local head 0
   int64_t vt_head;
   __bf16* kr;            // workspace rotated k, local head 0 (nullptr without RoPE)
   int64_t kr_head;
-  int32_t kv_len;
-  int32_t n_ktiles;      // ceil(kv_len / 64)
+  int32_t n_ktiles;      // ceil(max_b kv_len[b] / 64)
   int32_t hc;
+  int32_t batch;
   RopeGeom rope;
+  int32_t kv_len[kMaxBatch];
 };
 
 // Host-side launchers (defined in the kernel translation units).

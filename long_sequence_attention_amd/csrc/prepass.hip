@@ -25,9 +25,14 @@ __global__ void __launch_bounds__(256) prepare_kernel(PrepArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 tr[D * kPad];
 
   const int tile = blockIdx.x;
-  const int head = blockIdx.y;
+  const int bh = blockIdx.y;               // batch entry * hc + local head
+  const int bat = bh / a.hc;
+  const int head = bh - bat * a.hc;
   const int tid = threadIdx.x;
-  const __bf16* vsrc = a.v + (int64_t)head * a.kv_head;
+  const int kv_len = a.kv_len[bat];
+  // tiles past this entry's keys are never read by the attention kernel
+  if (tile * kBlockN >= kv_len) return;
+  const __bf16* vsrc = a.v + bat * a.kv_batch + (int64_t)head * a.kv_head;
 
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) {
@@ -36,13 +41,13 @@ __global__ void __launch_bounds__(256) prepare_kernel(PrepArgs a) {
     const int ch = qd % kChunks;
     const int key = tile * kBlockN + kl;
     bf16x8 v = bf16x8{};
-    if (key < a.kv_len) v = *reinterpret_cast<const bf16x8*>(vsrc + (int64_t)key * a.kv_row + ch * 8);
+    if (key < kv_len) v = *reinterpret_cast<const bf16x8*>(vsrc + (int64_t)key * a.kv_row + ch * 8);
     const int pos = vt_position(kl);
 #pragma unroll
     for (int e = 0; e < 8; ++e) tr[(ch * 8 + e) * kPad + pos] = (_Float16)(float)v[e];
   }
   __syncthreads();
-  _Float16* dst = a.vt + (int64_t)head * a.vt_head + (int64_t)tile * (D * kBlockN);
+  _Float16* dst = a.vt + (int64_t)bh * a.vt_head + (int64_t)tile * (D * kBlockN);
 #pragma unroll
   for (int i = 0; i < D * (kBlockN / 8) / 256; ++i) {
     const int qd = i * 256 + tid;
@@ -53,8 +58,8 @@ __global__ void __launch_bounds__(256) prepare_kernel(PrepArgs a) {
   }
 
   if constexpr (ROPE) {
-    const __bf16* ksrc = a.k + (int64_t)head * a.kv_head;
-    __bf16* kdst = a.kr + (int64_t)head * a.kr_head;
+    const __bf16* ksrc = a.k + bat * a.kv_batch + (int64_t)head * a.kv_head;
+    __bf16* kdst = a.kr + (int64_t)bh * a.kr_head;
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int qd = i * 256 + tid;
@@ -62,7 +67,7 @@ __global__ void __launch_bounds__(256) prepare_kernel(PrepArgs a) {
       const int ch = qd % kChunks;
       const int key = tile * kBlockN + kl;
       bf16x8 v = bf16x8{};
-      if (key < a.kv_len) {
+      if (key < kv_len) {
         v = *reinterpret_cast<const bf16x8*>(ksrc + (int64_t)key * a.kv_row + ch * 8);
         int t, y, x;
         rope_token_pos(a.rope, key, t, y, x);
@@ -105,14 +110,15 @@ __global__ void __launch_bounds__(256) rope_probe_kernel(RopeGeom g, int32_t nq,
 
 template <int D, bool ROPE>
 hipError_t launch_prepare_t(const PrepArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((prepare_kernel<D, ROPE>), dim3(a.n_ktiles, a.hc), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((prepare_kernel<D, ROPE>), dim3(a.n_ktiles, a.hc * a.batch), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_prepare(const PrepArgs& a, int head_dim, bool rope_k, hipStream_t s) {
-  if (a.n_ktiles <= 0 || a.hc <= 0 || a.hc > 65535) return hipErrorInvalidValue;
+  if (a.n_ktiles <= 0 || a.hc <= 0 || a.batch <= 0 || a.batch > kMaxBatch || (int64_t)a.hc * a.batch > 65535)
+    return hipErrorInvalidValue;
   if (head_dim == 128) return rope_k ? launch_prepare_t<128, true>(a, s) : launch_prepare_t<128, false>(a, s);
   if (head_dim == 64) return rope_k ? launch_prepare_t<64, true>(a, s) : launch_prepare_t<64, false>(a, s);
   return hipErrorInvalidValue;

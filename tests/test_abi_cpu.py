@@ -34,7 +34,7 @@ def header_functions():
 
 def test_library_exports_every_declared_symbol(lib):
     names = header_functions()
-    assert len(names) == 11
+    assert len(names) == 14
     assert sorted(names) == sorted(_lib.SIGNATURES)
     for n in names:
         assert hasattr(lib, n), n
@@ -105,10 +105,18 @@ ROPE = {"grid": (4, 32, 32), "dims": (44, 42, 42), "base": 10000.0}
     (dict(rope=dict(ROPE, base=0.0)), INVALID),
     (dict(rope=dict(ROPE, base=float("inf"))), INVALID),
     (dict(nk=512, rope=ROPE), INVALID),
+    (dict(batch=-1), INVALID),
+    (dict(batch=65), UNSUPPORTED),
+    (dict(batch=64, head_count=1025, heads_total=2048), UNSUPPORTED),
 ])
 def test_create_rejects_bad_descriptors(lib, kw, code):
     st, h = vd.create_raw(_desc(**kw))
     assert st == code and h == 0
+
+
+def test_batch_zero_reads_as_one():
+    # the field defaults to 0 in a zero-initialised descriptor; the binding passes 1
+    assert _lib.Desc().batch == 0 and _desc().batch == 1 and _desc(batch=2).batch == 2
 
 
 def test_create_rejects_null_arguments(lib):
@@ -127,6 +135,10 @@ def test_handle_checks_without_device(lib):
     assert lib.vdit_attn_fwd(bogus, None, None, None, 1, None, None, 0, None) == INVALID
     assert lib.vdit_attn_prepare(bogus, None, None, None, 1, None, 0, None) == INVALID
     assert lib.vdit_attn_attend(bogus, None, None, None, 1, None, None, 0, None) == INVALID
+    lens = (ctypes.c_int32 * 2)(5, 7)
+    assert lib.vdit_attn_fwd_lens(bogus, None, None, None, lens, None, None, 0, None) == INVALID
+    assert lib.vdit_attn_prepare_lens(bogus, None, None, None, lens, None, 0, None) == INVALID
+    assert lib.vdit_attn_attend_lens(bogus, None, None, None, lens, None, None, 0, None) == INVALID
     assert lib.vdit_attn_rope_probe(bogus, None, None) == INVALID
 
 
