@@ -85,20 +85,28 @@ struct FwdCfg {
                 "tiles must split into whole 1 KB direct loads per wave");
 };
 
-template <int D, int QB, int WAVES, bool ROPE>
+// NST = LDS stages per operand: 4 (K staged four and V^T two iterations ahead,
+// with the wave offset below) for one large workgroup per CU, or 2 (K two and
+// V^T one iteration ahead, 64 KB of LDS) so that two smaller workgroups share a
+// CU and one computes while the other waits on memory.
+template <int D, int QB, int WAVES, int NST, bool ROPE>
 __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   using C = FwdCfg<D, QB, WAVES>;
-  // Four K and four V^T stages, each its own array (not one array indexed by
-  // stage) so that the compiler can tell a direct load into one stage from
-  // reads of another and does not wait for the direct loads before LDS reads.
+  static_assert(NST == 4 || NST == 2, "stage count");
+  static_assert(NST == 2 || WAVES % 2 == 0, "the wave offset pairs waves w and w + WAVES/2");
+  // K and V^T stages, each its own array (not one array indexed by stage) so
+  // that the compiler can tell a direct load into one stage from reads of
+  // another and does not wait for the direct loads before LDS reads.
+  constexpr int kKHi = NST == 4 ? C::kKTile : 1024;  // stages 2, 3 (unused with NST = 2)
+  constexpr int kVHi = NST == 4 ? C::kVTile : 1024;
   __shared__ __attribute__((aligned(1024))) char k_st0[C::kKTile];
   __shared__ __attribute__((aligned(1024))) char k_st1[C::kKTile];
-  __shared__ __attribute__((aligned(1024))) char k_st2[C::kKTile];
-  __shared__ __attribute__((aligned(1024))) char k_st3[C::kKTile];
+  __shared__ __attribute__((aligned(1024))) char k_st2[kKHi];
+  __shared__ __attribute__((aligned(1024))) char k_st3[kKHi];
   __shared__ __attribute__((aligned(1024))) char v_st0[C::kVTile];
   __shared__ __attribute__((aligned(1024))) char v_st1[C::kVTile];
-  __shared__ __attribute__((aligned(1024))) char v_st2[C::kVTile];
-  __shared__ __attribute__((aligned(1024))) char v_st3[C::kVTile];
+  __shared__ __attribute__((aligned(1024))) char v_st2[kVHi];
+  __shared__ __attribute__((aligned(1024))) char v_st3[kVHi];
   __shared__ int wg_retry;
 
   // Workgroups are dispatched round-robin over the 8 XCDs; renumber them so that
@@ -359,15 +367,18 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   // direct loads issued per iteration by one wave
   constexpr int kPerIter = C::kKDma + C::kVDma;
 
-  // Stage tiles 0..1 (V) and 0..3 (K) and form the scores of tile 0.
+  // Stage the first tiles (K 0..3 and V 0..1, or K 0..1 and V 0 with two
+  // stages) and form the scores of tile 0.
   f32x16 s_a[QB][2], s_b[QB][2];
   auto prologue = [&]() {
     dma_k(0, k_st0);
     dma_v(0, v_st0);
     dma_k(1, k_st1);
-    dma_v(1, v_st1);
-    dma_k(2, k_st2);
-    dma_k(3, k_st3);
+    if constexpr (NST == 4) {
+      dma_v(1, v_st1);
+      dma_k(2, k_st2);
+      dma_k(3, k_st3);
+    }
     wait_vm<0>();
     barrier_only();
     scores(k_st0, s_a);
@@ -394,15 +405,22 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   // stay in flight. Staging indices past the last tile re-stage the last tile,
   // and the last iteration also forms scores it does not use, so the control
   // flow of every iteration is the same.
-  const bool upper = wave_u >= C::kWaves / 2;
+  //
+  // With NST = 2 there is no offset (the two waves of a SIMD belong to different
+  // workgroups): iteration t fills K(t+2) and V(t+1) and waits for all of them
+  // before its barrier.
+  const bool upper = NST == 4 && wave_u >= C::kWaves / 2;
   auto sync = [&]() {
-    wait_vm<C::kKDma + kPerIter>();
+    if constexpr (NST == 4)
+      wait_vm<C::kKDma + kPerIter>();
+    else
+      wait_vm<0>();
     barrier_only();
   };
   auto step = [&](int t, char* k_read, char* k_fill, char* v_read, char* v_fill, f32x16 (&s_cur)[QB][2],
                   f32x16 (&s_next)[QB][2], const float (&mref)[QB]) {
-    dma_v(t + 2, v_fill);
-    dma_k(t + 4, k_fill);
+    dma_v(t + NST / 2, v_fill);
+    dma_k(t + NST, k_fill);
     f16x8 vr[kR];
     f16x8 pf[QB][4];
     f16x2 hv[QB][kPairs];
@@ -419,11 +437,18 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int db = 0; db < C::kDB; ++db) o[qb][db] = f32x16{};
     }
-    for (int t = 0; t < ntiles; t += 4) {
-      step(t, k_st1, k_st0, v_st0, v_st2, s_a, s_b, mref);
-      if (t + 1 < ntiles) step(t + 1, k_st2, k_st1, v_st1, v_st3, s_b, s_a, mref);
-      if (t + 2 < ntiles) step(t + 2, k_st3, k_st2, v_st2, v_st0, s_a, s_b, mref);
-      if (t + 3 < ntiles) step(t + 3, k_st0, k_st3, v_st3, v_st1, s_b, s_a, mref);
+    if constexpr (NST == 4) {
+      for (int t = 0; t < ntiles; t += 4) {
+        step(t, k_st1, k_st0, v_st0, v_st2, s_a, s_b, mref);
+        if (t + 1 < ntiles) step(t + 1, k_st2, k_st1, v_st1, v_st3, s_b, s_a, mref);
+        if (t + 2 < ntiles) step(t + 2, k_st3, k_st2, v_st2, v_st0, s_a, s_b, mref);
+        if (t + 3 < ntiles) step(t + 3, k_st0, k_st3, v_st3, v_st1, s_b, s_a, mref);
+      }
+    } else {
+      for (int t = 0; t < ntiles; t += 2) {
+        step(t, k_st1, k_st0, v_st0, v_st1, s_a, s_b, mref);
+        if (t + 1 < ntiles) step(t + 1, k_st0, k_st1, v_st1, v_st0, s_b, s_a, mref);
+      }
     }
     // drain the direct loads still in flight before the stages are reused
     wait_vm<0>();
@@ -492,22 +517,36 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   }
 }
 
-template <int D, int QB, int WAVES, bool ROPE>
+template <int D, int QB, int WAVES, int NST, bool ROPE>
 hipError_t launch_fwd_t(AttnArgs a, hipStream_t s) {
   using C = FwdCfg<D, QB, WAVES>;
   a.n_qtiles = (a.nq + C::kBlockM - 1) / C::kBlockM;
   const int64_t nwg = (int64_t)a.n_qtiles * a.hc * a.batch;
   if (nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, QB, WAVES, ROPE>), dim3((unsigned)nwg), dim3(C::kThreads), 0, s, a);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, QB, WAVES, NST, ROPE>), dim3((unsigned)nwg), dim3(C::kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
+// Key lengths up to which the two-workgroups-per-CU configuration runs: with few
+// key tiles per workgroup its prologue and epilogue dominate, and a second
+// workgroup on the CU hides them.
+constexpr int kSmallKeys = 1024;
+
 hipError_t launch_attn_fwd(const AttnArgs& a, int head_dim, bool rope_q, hipStream_t s) {
   if (a.batch <= 0 || a.batch > kMaxBatch || a.hc <= 0) return hipErrorInvalidValue;
-  if (head_dim == 128) return rope_q ? launch_fwd_t<128, 1, 8, true>(a, s) : launch_fwd_t<128, 1, 8, false>(a, s);
-  if (head_dim == 64) return rope_q ? launch_fwd_t<64, 1, 8, true>(a, s) : launch_fwd_t<64, 1, 8, false>(a, s);
+  int max_len = 0;
+  for (int b = 0; b < a.batch; ++b) max_len = a.kv_len[b] > max_len ? a.kv_len[b] : max_len;
+  const bool small = max_len <= kSmallKeys;
+  if (head_dim == 128) {
+    if (small) return rope_q ? launch_fwd_t<128, 1, 4, 2, true>(a, s) : launch_fwd_t<128, 1, 4, 2, false>(a, s);
+    return rope_q ? launch_fwd_t<128, 1, 8, 4, true>(a, s) : launch_fwd_t<128, 1, 8, 4, false>(a, s);
+  }
+  if (head_dim == 64) {
+    if (small) return rope_q ? launch_fwd_t<64, 1, 4, 2, true>(a, s) : launch_fwd_t<64, 1, 4, 2, false>(a, s);
+    return rope_q ? launch_fwd_t<64, 1, 8, 4, true>(a, s) : launch_fwd_t<64, 1, 8, 4, false>(a, s);
+  }
   return hipErrorInvalidValue;
 }
 
