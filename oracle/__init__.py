@@ -19,6 +19,9 @@ Everything here is plain float64 numpy, written from the definitions:
     not state this formula; it is the reading documented with the functions.
   * ``ulysses_head_range``: the head share of one rank (same section, and the
     divisibility rule in "Tuning cost and GPU count").
+  * ``int8_qk``: attention on q and k quantized to int8 per block (the
+    ``per_block_int8`` step of SageAttention in the same ComfyUI traceback), with
+    every code decided in float32 as the library decides it.
 
 Parity status of each function is stated in its docstring.
 """
@@ -32,4 +35,8 @@ from .attention import (  # noqa: F401
     attention_weights,
     attention_rows,
     mha_reference,
+)
+from .int8_qk import (  # noqa: F401
+    quantize_blocks,
+    mha_reference_qk_int8,
 )
