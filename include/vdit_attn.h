@@ -102,6 +102,20 @@ typedef enum {
  *                   at most 65535, else UNSUPPORTED). Shapes below then read
  *                   q [B, nq, Ht, d], k and v [B, nk, Ht, d], packed [B, n, 3, Ht, d],
  *                   out [B, nq, head_count, d].
+ *   qk_int8         1: q.k on int8 codes, quantized per block by prepare (the per-block
+ *                   int8 step that the WAN forward pass runs through SageAttention,
+ *                   ComfyUI issue "MultiGPU Work Units": per_block_int8(q, k, sm_scale)).
+ *                   Reading: symmetric codes, one scale per block of 128 query / 64 key
+ *                   tokens of one (entry, head), q multiplied by the softmax scale first;
+ *                   scale = amax / 127 (float32, IEEE division; 1 if below 2^-100),
+ *                   code = round-half-even(x / scale) clamped to [-127, 127]; scores =
+ *                   q scale * k scale * integer dot product. Softmax and the weighted sum
+ *                   are as without it. Needs d = 128, no RoPE and nk <= 262144
+ *                   (UNSUPPORTED otherwise). Workspace with qk_int8, after the regions
+ *                   below, each region starting at the next multiple of 256 bytes:
+ *                   q codes int8 [B * head_count][ceil(nq/128)*128][d], k codes int8
+ *                   [B * head_count][ceil(nk/64)*64][d], q scales float
+ *                   [B * head_count][ceil(nq/128)], k scales float [B * head_count][ceil(nk/64)].
  */
 typedef struct {
   int32_t nq;
@@ -118,6 +132,7 @@ typedef struct {
   int32_t rope_dim_t, rope_dim_h, rope_dim_w;
   double rope_base;
   int32_t batch;
+  int32_t qk_int8;
 } vdit_attn_desc_t;
 
 /*
@@ -175,7 +190,8 @@ vdit_status_t vdit_attn_fwd(vdit_attn_t h, const void* q, const void* k, const v
 /*
  * First stage of fwd: writes v (heads of the share, keys < key_len) transposed
  * and converted to float16 into the workspace, zero-filled up to the next
- * multiple of 64 keys; with use_rope also the rotated keys (bfloat16). Arguments
+ * multiple of 64 keys; with use_rope also the rotated keys (bfloat16); with
+ * qk_int8 the int8 codes and scales of q and of the valid keys. Arguments
  * as for fwd (q is read only for the N3HD layout, where it is the packed tensor).
  */
 vdit_status_t vdit_attn_prepare(vdit_attn_t h, const void* q, const void* k, const void* v,

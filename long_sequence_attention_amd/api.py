@@ -62,9 +62,10 @@ def ulysses_heads(heads_total: int, degree: int, rank: int) -> tuple[int, int]:
 
 def make_desc(nq: int, nk: int, heads_total: int, head_dim: int, *, layout: str = "NHD", head_begin: int = 0,
               head_count: int | None = None, scale: float = 0.0, use_key_mask: bool = False,
-              rope: dict | None = None, batch: int = 1) -> _lib.Desc:
+              rope: dict | None = None, batch: int = 1, qk_int8: bool = False) -> _lib.Desc:
     d = _lib.Desc()
     d.batch = batch
+    d.qk_int8 = 1 if qk_int8 else 0
     d.nq, d.nk, d.heads_total, d.head_dim = nq, nk, heads_total, head_dim
     d.layout = {"NHD": _lib.LAYOUT_NHD, "N3HD": _lib.LAYOUT_N3HD}[layout]
     d.head_begin = head_begin
@@ -90,16 +91,18 @@ class Attention:
     """One attention plan (vdit_attn_t) and its calls on torch tensors.
 
     With ``batch`` = B > 1 every tensor has a leading [B] dimension; the calls take
-    either one ``key_len`` for all entries or ``key_lens`` (B values).
+    either one ``key_len`` for all entries or ``key_lens`` (B values). ``qk_int8``
+    selects q.k on int8 per-block codes (d = 128, no RoPE).
     """
 
     def __init__(self, nq: int, nk: int, heads_total: int, head_dim: int, *, layout: str = "NHD",
                  head_begin: int = 0, head_count: int | None = None, scale: float = 0.0,
-                 use_key_mask: bool = False, rope: dict | None = None, batch: int = 1):
+                 use_key_mask: bool = False, rope: dict | None = None, batch: int = 1,
+                 qk_int8: bool = False):
         self._lib = _lib.load()
         self.desc = make_desc(nq, nk, heads_total, head_dim, layout=layout, head_begin=head_begin,
                               head_count=head_count, scale=scale, use_key_mask=use_key_mask, rope=rope,
-                              batch=batch)
+                              batch=batch, qk_int8=qk_int8)
         self.layout = layout
         self.batch = int(batch)
         h = ctypes.c_void_p()

@@ -18,6 +18,9 @@ struct vdit_attn {
   int64_t nk_pad;      // keys rounded up to the key tile
   size_t ws_vt_off, ws_vt_bytes;
   size_t ws_kr_off, ws_kr_bytes;
+  // int8 q.k: codes and scales per (entry, head)
+  int64_t nq_pad;      // queries rounded up to the q quantization block
+  size_t ws_qc_off, ws_kc_off, ws_qs_off, ws_ks_off;
   size_t ws_total;
   float2* rope_tab;    // device (cos, sin) table, or nullptr
   vdit::RopeGeom geom;
@@ -62,6 +65,9 @@ vdit_status_t validate_desc(const vdit_attn_desc_t& d) {
   if (std::isnan(d.scale) || std::isinf(d.scale)) return VDIT_ERR_INVALID_ARG;
   if (d.use_key_mask != 0 && d.use_key_mask != 1) return VDIT_ERR_INVALID_ARG;
   if (d.use_rope != 0 && d.use_rope != 1) return VDIT_ERR_INVALID_ARG;
+  if (d.qk_int8 != 0 && d.qk_int8 != 1) return VDIT_ERR_INVALID_ARG;
+  if (d.qk_int8 && (d.head_dim != 128 || d.use_rope || d.nk > vdit::kQK8MaxTiles * vdit::kBlockN))
+    return VDIT_ERR_UNSUPPORTED;
   // element offsets are 64-bit in the kernels; keep every tensor below 2^60 elements
   const int64_t row = (int64_t)d.heads_total * d.head_dim * (d.layout == VDIT_LAYOUT_N3HD ? 3 : 1);
   const int64_t nmax = d.nq > d.nk ? d.nq : d.nk;
@@ -205,6 +211,31 @@ vdit_status_t do_prepare(const vdit_attn& h, const Inputs& in, const KeyLens& kl
   a.rope = h.geom;
   for (int32_t b = 0; b < vdit::kMaxBatch; ++b) a.kv_len[b] = kl.len[b];
   if (vdit::launch_prepare(a, d.head_dim, d.use_rope != 0, s) != hipSuccess) return VDIT_ERR_DEVICE;
+  if (d.qk_int8) {
+    char* w = static_cast<char*>(ws);
+    vdit::QuantArgs qa{};
+    qa.q = in.q;
+    qa.k = in.k;
+    qa.q_row = in.q_row;
+    qa.k_row = in.kv_row;
+    qa.q_batch = in.q_batch;
+    qa.k_batch = in.kv_batch;
+    qa.head = d.head_dim;
+    qa.qc = reinterpret_cast<int8_t*>(w + h.ws_qc_off);
+    qa.kc = reinterpret_cast<int8_t*>(w + h.ws_kc_off);
+    qa.qc_bh = h.nq_pad * d.head_dim;
+    qa.kc_bh = h.nk_pad * d.head_dim;
+    qa.qsc = reinterpret_cast<float*>(w + h.ws_qs_off);
+    qa.ksc = reinterpret_cast<float*>(w + h.ws_ks_off);
+    qa.nq = d.nq;
+    qa.nq_blocks = (int32_t)(h.nq_pad / vdit::kQuantQ);
+    qa.nk_blocks = (int32_t)(h.nk_pad / vdit::kQuantK);
+    qa.hc = d.head_count;
+    qa.batch = d.batch;
+    qa.sm_scale = h.scale;
+    for (int32_t b = 0; b < vdit::kMaxBatch; ++b) qa.kv_len[b] = kl.len[b];
+    if (vdit::launch_quantize(qa, d.head_dim, s) != hipSuccess) return VDIT_ERR_DEVICE;
+  }
   return VDIT_OK;
 }
 
@@ -237,8 +268,21 @@ vdit_status_t do_attend(const vdit_attn& h, const Inputs& in, const KeyLens& kl,
   a.batch = d.batch;
   a.c = h.c;
   a.rope = h.geom;
+  if (d.qk_int8) {
+    const char* w = static_cast<const char*>(ws);
+    a.c = 1.4426950408889634f;  // log2(e): the softmax scale is inside the q codes
+    a.qc = reinterpret_cast<const int8_t*>(w + h.ws_qc_off);
+    a.kc = reinterpret_cast<const int8_t*>(w + h.ws_kc_off);
+    a.qc_bh = h.nq_pad * d.head_dim;
+    a.kc_bh = h.nk_pad * d.head_dim;
+    a.qsc = reinterpret_cast<const float*>(w + h.ws_qs_off);
+    a.ksc = reinterpret_cast<const float*>(w + h.ws_ks_off);
+    a.nq_blocks = (int32_t)(h.nq_pad / vdit::kQuantQ);
+    a.nk_blocks = (int32_t)(h.nk_pad / vdit::kQuantK);
+  }
   for (int32_t b = 0; b < vdit::kMaxBatch; ++b) a.kv_len[b] = kl.len[b];
-  if (vdit::launch_attn_fwd(a, d.head_dim, d.use_rope != 0, s) != hipSuccess) return VDIT_ERR_DEVICE;
+  if (vdit::launch_attn_fwd(a, d.head_dim, d.use_rope != 0, d.qk_int8 != 0, s) != hipSuccess)
+    return VDIT_ERR_DEVICE;
   return VDIT_OK;
 }
 
@@ -296,6 +340,15 @@ vdit_status_t vdit_attn_create(const vdit_attn_desc_t* desc, vdit_attn_t* out) {
   h.ws_kr_off = align_up(h.ws_vt_bytes, 256);
   h.ws_kr_bytes = d.use_rope ? per_head * d.head_count * d.batch : 0;
   h.ws_total = d.use_rope ? h.ws_kr_off + h.ws_kr_bytes : h.ws_vt_bytes;
+  h.nq_pad = ((int64_t)d.nq + vdit::kQuantQ - 1) / vdit::kQuantQ * vdit::kQuantQ;
+  if (d.qk_int8) {
+    const size_t slices = (size_t)d.head_count * d.batch;
+    h.ws_qc_off = align_up(h.ws_total, 256);
+    h.ws_kc_off = align_up(h.ws_qc_off + slices * h.nq_pad * d.head_dim, 256);
+    h.ws_qs_off = align_up(h.ws_kc_off + slices * h.nk_pad * d.head_dim, 256);
+    h.ws_ks_off = align_up(h.ws_qs_off + slices * (h.nq_pad / vdit::kQuantQ) * sizeof(float), 256);
+    h.ws_total = h.ws_ks_off + slices * (h.nk_pad / vdit::kQuantK) * sizeof(float);
+  }
   h.rope_tab = nullptr;
   h.geom = vdit::RopeGeom{};
 

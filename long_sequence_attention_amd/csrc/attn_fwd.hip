@@ -67,19 +67,19 @@ __device__ __forceinline__ uint32_t lds_addr(const char* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
 }
 
-template <int D, int QB, int WAVES>
+template <int D, int QB, int WAVES, bool QK8 = false>
 struct FwdCfg {
   static constexpr int kWaves = WAVES;
   static constexpr int kThreads = kWaves * kWave;
   static constexpr int kBlockM = kWaves * QB * 32;
-  static constexpr int kKChunks = D / 8;                 // 16-byte chunks per K row
-  static constexpr int kKRow = D * 2;                    // bytes per K row in LDS
+  static constexpr int kKRow = QK8 ? D : D * 2;          // bytes per K row in LDS (int8 or bf16)
+  static constexpr int kKChunks = kKRow / 16;            // 16-byte chunks per K row
   static constexpr int kVRow = kBlockN * 2;              // bytes per V^T row in LDS
   static constexpr int kKTile = kBlockN * kKRow;         // bytes
   static constexpr int kVTile = D * kVRow;               // bytes
   static constexpr int kKDma = kKTile / 1024 / kWaves;   // 1 KB direct loads per wave per K tile
   static constexpr int kVDma = kVTile / 1024 / kWaves;
-  static constexpr int kDK = D / 16;                     // MFMA k-steps over d
+  static constexpr int kDK = QK8 ? D / 32 : D / 16;     // q.k MFMA k-steps over d (16 bytes per lane)
   static constexpr int kDB = D / 32;                     // 32-row blocks of d
   static_assert(kKDma >= 1 && kVDma >= 1 && kKDma * kWaves * 1024 == kKTile && kVDma * kWaves * 1024 == kVTile,
                 "tiles must split into whole 1 KB direct loads per wave");
@@ -89,9 +89,16 @@ struct FwdCfg {
 // with the wave offset below) for one large workgroup per CU, or 2 (K two and
 // V^T one iteration ahead, 64 KB of LDS) so that two smaller workgroups share a
 // CU and one computes while the other waits on memory.
-template <int D, int QB, int WAVES, int NST, bool ROPE>
+// QK8: q.k on int8 codes per block (v_mfma_i32_32x32x32_i8), prepared by the
+// quantize pre-pass with the softmax scale folded into q. The integer scores of
+// the next tile are converted to float during the weight products; each tile's
+// weights then use c = q scale * k scale * log2 e per lane, so the softmax costs
+// one conversion per score more than with bfloat16 q.k.
+template <int D, int QB, int WAVES, int NST, bool ROPE, bool QK8>
 __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
-  using C = FwdCfg<D, QB, WAVES>;
+  using C = FwdCfg<D, QB, WAVES, QK8>;
+  using QFrag = typename std::conditional<QK8, i32x4, bf16x8>::type;
+  static_assert(!(QK8 && ROPE), "int8 q.k takes no RoPE");
   static_assert(NST == 4 || NST == 2, "stage count");
   static_assert(NST == 2 || WAVES % 2 == 0, "the wave offset pairs waves w and w + WAVES/2");
   // K and V^T stages, each its own array (not one array indexed by stage) so
@@ -108,6 +115,8 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char v_st2[kVHi];
   __shared__ __attribute__((aligned(1024))) char v_st3[kVHi];
   __shared__ int wg_retry;
+  // int8 q.k: k scale of every key tile of this (entry, head), copied in the prologue
+  __shared__ float ks_lds[QK8 ? (NST == 4 ? kQK8MaxTiles : kSmallKeys / kBlockN) : 1];
 
   // Workgroups are dispatched round-robin over the 8 XCDs; renumber them so that
   // each XCD walks a contiguous range of (head, query tile) and its L2 serves the
@@ -133,32 +142,55 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
 
   // ---- this wave's queries into registers (B operand layout), RoPE fused
   const int q0 = qtile * C::kBlockM + wave * QB * 32;
-  bf16x8 qf[QB][C::kDK];
+  QFrag qf[QB][C::kDK];
+  float cq[QB];  // factor of the float scores in the exponent (log2 domain)
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int qi = q0 + qb * 32 + l32;
+    cq[qb] = a.c;
     if (qi < a.nq) {
-      const __bf16* qp = a.q + bat * a.q_batch + (int64_t)qi * a.q_row + (int64_t)head * a.q_head + 8 * hl;
-      int t = 0, y = 0, x = 0;
-      if constexpr (ROPE) rope_token_pos(a.rope, qi, t, y, x);
+      if constexpr (QK8) {
+        // lane half h holds dims [32 kk + 16 h, 32 kk + 16 h + 16) of k-step kk
+        const int8_t* qp = a.qc + bh * a.qc_bh + (int64_t)qi * D + 16 * hl;
 #pragma unroll
-      for (int kk = 0; kk < C::kDK; ++kk) {
-        bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + 16 * kk);
-        if constexpr (ROPE) v = rope_chunk(a.rope, v, 16 * kk + 8 * hl, t, y, x);
-        qf[qb][kk] = v;
+        for (int kk = 0; kk < C::kDK; ++kk) qf[qb][kk] = *reinterpret_cast<const i32x4*>(qp + 32 * kk);
+        cq[qb] = a.qsc[(int64_t)bh * a.nq_blocks + qi / kQuantQ] * a.c;
+      } else {
+        const __bf16* qp = a.q + bat * a.q_batch + (int64_t)qi * a.q_row + (int64_t)head * a.q_head + 8 * hl;
+        int t = 0, y = 0, x = 0;
+        if constexpr (ROPE) rope_token_pos(a.rope, qi, t, y, x);
+#pragma unroll
+        for (int kk = 0; kk < C::kDK; ++kk) {
+          bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + 16 * kk);
+          if constexpr (ROPE) v = rope_chunk(a.rope, v, 16 * kk + 8 * hl, t, y, x);
+          qf[qb][kk] = v;
+        }
       }
     } else {
 #pragma unroll
-      for (int kk = 0; kk < C::kDK; ++kk) qf[qb][kk] = bf16x8{};
+      for (int kk = 0; kk < C::kDK; ++kk) qf[qb][kk] = QFrag{};
     }
   }
 
   const int kv_len = a.kv_len[bat];
   const int ntiles = (kv_len + kBlockN - 1) / kBlockN;
-  const float c = a.c;
-  const char* kbytes = reinterpret_cast<const char*>(a.k + bat * a.k_batch + (int64_t)head * a.k_head);
+  const char* kbytes = QK8 ? reinterpret_cast<const char*>(a.kc + bh * a.kc_bh)
+                           : reinterpret_cast<const char*>(a.k + bat * a.k_batch + (int64_t)head * a.k_head);
   const char* vbytes = reinterpret_cast<const char*>(a.vt + bat * a.vt_batch + (int64_t)head * a.vt_head);
-  const int krow_bytes = (int)(a.k_row * 2);
+  const int krow_bytes = QK8 ? D : (int)(a.k_row * 2);
+  // factor of tile t's float scores in the exponent: c, or with int8 q.k
+  // q scale * k scale * log2 e (at least FLT_MIN, so that masked scores stay -inf).
+  // The k scales are read from LDS: a global load here would make the compiler
+  // wait for every direct load in flight.
+  auto tile_c = [&](int t, float (&ct)[QB]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      if constexpr (QK8)
+        ct[qb] = fmaxf(cq[qb] * ks_lds[min(t, ntiles - 1)], 0x1p-126f);
+      else
+        ct[qb] = cq[qb];
+    }
+  };
 
   // ---- direct global -> LDS staging. Wave w fills the 1 KB pieces w*n .. w*n+n-1
   // of a tile; lane l writes bytes [16 l, 16 l + 16) of a piece, i.e. the LDS
@@ -213,6 +245,15 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   }
 
   // S^T = K * Q^T for the K tile in `kl`
+  // one q.k product: bfloat16, or int8 with the int32 accumulator carried in the
+  // bits of the float vector until it is converted
+  auto qk_mfma = [](const QFrag& ka, const QFrag& qv, f32x16 acc) -> f32x16 {
+    if constexpr (QK8)
+      return __builtin_bit_cast(
+          f32x16, __builtin_amdgcn_mfma_i32_32x32x32_i8(ka, qv, __builtin_bit_cast(i32x16, acc), 0, 0, 0));
+    else
+      return __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qv, acc, 0, 0, 0);
+  };
   auto scores = [&](const char* kl, f32x16 (&s)[QB][2]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) { s[qb][0] = f32x16{}; s[qb][1] = f32x16{}; }
@@ -220,11 +261,22 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
     for (int kk = 0; kk < C::kDK; ++kk) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kl + kb * 32 * C::kKRow + koff[kk]);
+        const QFrag ka = *reinterpret_cast<const QFrag*>(kl + kb * 32 * C::kKRow + koff[kk]);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[qb][kk], s[qb][kb], 0, 0, 0);
+        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = qk_mfma(ka, qf[qb][kk], s[qb][kb]);
       }
+    }
+    if constexpr (QK8) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const i32x16 iv = __builtin_bit_cast(i32x16, s[qb][kb]);
+          f32x16 fv;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) fv[r] = (float)iv[r];
+          s[qb][kb] = fv;
+        }
     }
   };
   // scores of keys past kv_len to -inf (only the last tile can hold such keys)
@@ -245,7 +297,7 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
     }
   };
   // maximum of the scores of each query in the tile (both lane halves), times c
-  auto tile_max = [&](const f32x16 (&s)[QB][2], float (&m)[QB]) {
+  auto tile_max = [&](const f32x16 (&s)[QB][2], const float (&ct)[QB], float (&m)[QB]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float mx = s[qb][0][0];
@@ -254,7 +306,7 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][1][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      m[qb] = mx * c;
+      m[qb] = mx * ct[qb];
     }
   };
 
@@ -282,7 +334,7 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   constexpr int kPPG = kPairs / kNS;         // pairs per score product
   static_assert(kNS >= kR && kNP >= kR && kPairs % kNS == 0 && kPairs % kNP == 0, "pipeline shape");
   auto kfrag = [&](const char* kl, int j) {
-    return *reinterpret_cast<const bf16x8*>(kl + (j & 1) * 32 * C::kKRow + koff[j >> 1]);
+    return *reinterpret_cast<const QFrag*>(kl + (j & 1) * 32 * C::kKRow + koff[j >> 1]);
   };
   auto vfrag = [&](const char* vl, int j) {
     return *reinterpret_cast<const f16x8*>(vl + (j % C::kDB) * 32 * C::kVRow + voff[j / C::kDB]);
@@ -290,9 +342,9 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   // scores of the next tile with the weights of the held one; leaves the first
   // kR V^T fragments of the products in `vr`
   auto score_phase = [&](const char* k_read, const char* v_read, const f32x16 (&s_cur)[QB][2],
-                         f32x16 (&s_next)[QB][2], const float (&mref)[QB], f16x8 (&vr)[kR], f16x8 (&pf)[QB][4],
-                         f16x2 (&hv)[QB][kPairs]) {
-    bf16x8 kr[kR];
+                         f32x16 (&s_next)[QB][2], const float (&ccur)[QB], const float (&mref)[QB],
+                         f16x8 (&vr)[kR], f16x8 (&pf)[QB][4], f16x2 (&hv)[QB][kPairs]) {
+    QFrag kr[kR];
     u32x4 bits[QB][4];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -307,7 +359,7 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
       const int kk = g >> 1, kb = g & 1;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
-        s_next[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[g % kR], qf[qb][kk], s_next[qb][kb], 0, 0, 0);
+        s_next[qb][kb] = qk_mfma(kr[g % kR], qf[qb][kk], s_next[qb][kb]);
       if (g + kR < kNS)
         kr[g % kR] = kfrag(k_read, g + kR);
       else
@@ -320,8 +372,8 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
         for (int qb = 0; qb < QB; ++qb) {
           const float nm = -mref[qb];
           f16x2 h2;
-          h2[0] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[qb][skb][r], c, nm));
-          h2[1] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[qb][skb][r + 1], c, nm));
+          h2[0] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[qb][skb][r], ccur[qb], nm));
+          h2[1] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[qb][skb][r + 1], ccur[qb], nm));
           uint32_t u = __builtin_bit_cast(uint32_t, h2);
           asm volatile("" : "+v"(u));  // keeps the weights in this group
           hv[qb][p] = __builtin_bit_cast(f16x2, u);
@@ -337,8 +389,10 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   };
   // O^T += V^T P^T; the row sums of the rounded weights (v_dot2) ride along with
   // the products, which have no other vector work
+  // with int8 q.k this also converts the integer scores of the next tile to
+  // float, two per product
   auto product_phase = [&](const char* v_read, f16x8 (&vr)[kR], const f16x8 (&pf)[QB][4],
-                           const f16x2 (&hv)[QB][kPairs]) {
+                           const f16x2 (&hv)[QB][kPairs], f32x16 (&s_next)[QB][2]) {
     float lsum[QB][4];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
@@ -358,6 +412,18 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
           lsum[qb][p >> 2] = __builtin_amdgcn_fdot2(hv[qb][p], ones, lsum[qb][p >> 2], false);
           asm volatile("" : "+v"(lsum[qb][p >> 2]));  // keeps the sum in this group
         }
+      if constexpr (QK8) {
+        static_assert(32 % kNP == 0, "conversions per product");
+#pragma unroll
+        for (int e = g * (32 / kNP); e < (g + 1) * (32 / kNP); ++e)
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            const i32x16 iv = __builtin_bit_cast(i32x16, s_next[qb][e >> 4]);
+            float f = (float)iv[e & 15];
+            asm volatile("" : "+v"(f));  // keeps the conversion in this group
+            s_next[qb][e >> 4][e & 15] = f;
+          }
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
@@ -370,7 +436,12 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   // Stage the first tiles (K 0..3 and V 0..1, or K 0..1 and V 0 with two
   // stages) and form the scores of tile 0.
   f32x16 s_a[QB][2], s_b[QB][2];
+  float c_a[QB], c_b[QB];
   auto prologue = [&]() {
+    if constexpr (QK8) {
+      const float* ksrc = a.ksc + (int64_t)bh * a.nk_blocks;
+      for (int i = tid; i < ntiles; i += C::kThreads) ks_lds[i] = ksrc[i];
+    }
     dma_k(0, k_st0);
     dma_v(0, v_st0);
     dma_k(1, k_st1);
@@ -383,6 +454,7 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
     barrier_only();
     scores(k_st0, s_a);
     mask_tail(0, s_a);
+    tile_c(0, c_a);
     // every wave has read stage 0 before iteration 0 refills it
     barrier_only();
   };
@@ -417,17 +489,20 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
       wait_vm<0>();
     barrier_only();
   };
+  // c_cur / c_next: exponent factors of the scores held for tiles t and t+1
   auto step = [&](int t, char* k_read, char* k_fill, char* v_read, char* v_fill, f32x16 (&s_cur)[QB][2],
-                  f32x16 (&s_next)[QB][2], const float (&mref)[QB]) {
+                  f32x16 (&s_next)[QB][2], const float (&c_cur)[QB], float (&c_next)[QB],
+                  const float (&mref)[QB]) {
     dma_v(t + NST / 2, v_fill);
     dma_k(t + NST, k_fill);
     f16x8 vr[kR];
     f16x8 pf[QB][4];
     f16x2 hv[QB][kPairs];
-    score_phase(k_read, v_read, s_cur, s_next, mref, vr, pf, hv);
+    score_phase(k_read, v_read, s_cur, s_next, c_cur, mref, vr, pf, hv);
     if (upper) sync();
-    product_phase(v_read, vr, pf, hv);
+    product_phase(v_read, vr, pf, hv, s_next);
     mask_tail(t + 1, s_next);
+    tile_c(t + 1, c_next);
     if (!upper) sync();
   };
   auto main_pass = [&](const float (&mref)[QB]) {
@@ -439,15 +514,15 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
     }
     if constexpr (NST == 4) {
       for (int t = 0; t < ntiles; t += 4) {
-        step(t, k_st1, k_st0, v_st0, v_st2, s_a, s_b, mref);
-        if (t + 1 < ntiles) step(t + 1, k_st2, k_st1, v_st1, v_st3, s_b, s_a, mref);
-        if (t + 2 < ntiles) step(t + 2, k_st3, k_st2, v_st2, v_st0, s_a, s_b, mref);
-        if (t + 3 < ntiles) step(t + 3, k_st0, k_st3, v_st3, v_st1, s_b, s_a, mref);
+        step(t, k_st1, k_st0, v_st0, v_st2, s_a, s_b, c_a, c_b, mref);
+        if (t + 1 < ntiles) step(t + 1, k_st2, k_st1, v_st1, v_st3, s_b, s_a, c_b, c_a, mref);
+        if (t + 2 < ntiles) step(t + 2, k_st3, k_st2, v_st2, v_st0, s_a, s_b, c_a, c_b, mref);
+        if (t + 3 < ntiles) step(t + 3, k_st0, k_st3, v_st3, v_st1, s_b, s_a, c_b, c_a, mref);
       }
     } else {
       for (int t = 0; t < ntiles; t += 2) {
-        step(t, k_st1, k_st0, v_st0, v_st1, s_a, s_b, mref);
-        if (t + 1 < ntiles) step(t + 1, k_st0, k_st1, v_st1, v_st0, s_b, s_a, mref);
+        step(t, k_st1, k_st0, v_st0, v_st1, s_a, s_b, c_a, c_b, mref);
+        if (t + 1 < ntiles) step(t + 1, k_st0, k_st1, v_st1, v_st0, s_b, s_a, c_b, c_a, mref);
       }
     }
     // drain the direct loads still in flight before the stages are reused
@@ -458,7 +533,7 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   // ---- reference maximum from the first key tile
   prologue();
   float mref[QB];
-  tile_max(s_a, mref);
+  tile_max(s_a, c_a, mref);
   main_pass(mref);
 
   // ---- rare path: some weight left the float16 range (a later key scored far
@@ -486,8 +561,9 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
       f32x16 s[QB][2];
       scores(k_st0, s);
       mask_tail(t, s);
-      float m[QB];
-      tile_max(s, m);
+      float ct[QB], m[QB];
+      tile_c(t, ct);
+      tile_max(s, ct, m);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) mx[qb] = fmaxf(mx[qb], m[qb]);
       __syncthreads();
@@ -517,35 +593,37 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   }
 }
 
-template <int D, int QB, int WAVES, int NST, bool ROPE>
+template <int D, int QB, int WAVES, int NST, bool ROPE, bool QK8>
 hipError_t launch_fwd_t(AttnArgs a, hipStream_t s) {
-  using C = FwdCfg<D, QB, WAVES>;
+  using C = FwdCfg<D, QB, WAVES, QK8>;
   a.n_qtiles = (a.nq + C::kBlockM - 1) / C::kBlockM;
   const int64_t nwg = (int64_t)a.n_qtiles * a.hc * a.batch;
   if (nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, QB, WAVES, NST, ROPE>), dim3((unsigned)nwg), dim3(C::kThreads), 0, s, a);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, QB, WAVES, NST, ROPE, QK8>), dim3((unsigned)nwg), dim3(C::kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// Key lengths up to which the two-workgroups-per-CU configuration runs: with few
-// key tiles per workgroup its prologue and epilogue dominate, and a second
-// workgroup on the CU hides them.
-constexpr int kSmallKeys = 1024;
 
-hipError_t launch_attn_fwd(const AttnArgs& a, int head_dim, bool rope_q, hipStream_t s) {
+hipError_t launch_attn_fwd(const AttnArgs& a, int head_dim, bool rope_q, bool qk_int8, hipStream_t s) {
   if (a.batch <= 0 || a.batch > kMaxBatch || a.hc <= 0) return hipErrorInvalidValue;
   int max_len = 0;
   for (int b = 0; b < a.batch; ++b) max_len = a.kv_len[b] > max_len ? a.kv_len[b] : max_len;
   const bool small = max_len <= kSmallKeys;
+  if (qk_int8) {
+    if (head_dim != 128 || rope_q) return hipErrorInvalidValue;
+    return small ? launch_fwd_t<128, 1, 4, 2, false, true>(a, s) : launch_fwd_t<128, 1, 8, 4, false, true>(a, s);
+  }
   if (head_dim == 128) {
-    if (small) return rope_q ? launch_fwd_t<128, 1, 4, 2, true>(a, s) : launch_fwd_t<128, 1, 4, 2, false>(a, s);
-    return rope_q ? launch_fwd_t<128, 1, 8, 4, true>(a, s) : launch_fwd_t<128, 1, 8, 4, false>(a, s);
+    if (small)
+      return rope_q ? launch_fwd_t<128, 1, 4, 2, true, false>(a, s) : launch_fwd_t<128, 1, 4, 2, false, false>(a, s);
+    return rope_q ? launch_fwd_t<128, 1, 8, 4, true, false>(a, s) : launch_fwd_t<128, 1, 8, 4, false, false>(a, s);
   }
   if (head_dim == 64) {
-    if (small) return rope_q ? launch_fwd_t<64, 1, 4, 2, true>(a, s) : launch_fwd_t<64, 1, 4, 2, false>(a, s);
-    return rope_q ? launch_fwd_t<64, 1, 8, 4, true>(a, s) : launch_fwd_t<64, 1, 8, 4, false>(a, s);
+    if (small)
+      return rope_q ? launch_fwd_t<64, 1, 4, 2, true, false>(a, s) : launch_fwd_t<64, 1, 4, 2, false, false>(a, s);
+    return rope_q ? launch_fwd_t<64, 1, 8, 4, true, false>(a, s) : launch_fwd_t<64, 1, 8, 4, false, false>(a, s);
   }
   return hipErrorInvalidValue;
 }

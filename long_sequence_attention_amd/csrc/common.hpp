@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace vdit {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -12,6 +14,8 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));    // 16 int8 codes
+typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kWave = 64;
 constexpr int kBlockN = 64;  // keys per K/V tile
@@ -87,6 +91,18 @@ __device__ __forceinline__ bf16x8 rope_chunk(const RopeGeom& g, bf16x8 v, int32_
 // Sequences per call (batch entries) whose key lengths travel in the launch arguments.
 constexpr int kMaxBatch = 64;
 
+// Blocks of the int8 quantization of q and k: one scale per block of consecutive
+// tokens of one (entry, head).
+constexpr int kQuantQ = 128;
+constexpr int kQuantK = 64;  // equals kBlockN: one k scale per key tile
+// Key tiles whose k scales fit the attention kernel's LDS table (int8 q.k).
+constexpr int kQK8MaxTiles = 4096;
+
+// Key lengths up to which the attention runs two smaller workgroups per CU: with
+// few key tiles per workgroup its prologue and epilogue dominate, and a second
+// workgroup on the CU hides them.
+constexpr int kSmallKeys = 1024;
+
 // Element offsets of batch entry b are b * (the *_batch stride) on top of those below.
 struct AttnArgs {
   const __bf16* q;       // q of head `head_begin`, token 0, entry 0
@@ -108,7 +124,37 @@ struct AttnArgs {
   float c;               // scale * log2(e)
   int32_t q_head;        // elements between consecutive heads of q (= d)
   RopeGeom rope;
+  // int8 q.k (workspace, laid out per (entry, head) = bh): codes [bh][tokens][d],
+  // scales [bh][blocks]
+  const int8_t* qc;      // q codes (q already multiplied by the softmax scale)
+  const int8_t* kc;      // k codes, [bh][nk_pad][d]
+  int64_t qc_bh;         // elements between (entry, head) slices of qc
+  int64_t kc_bh;
+  const float* qsc;      // q scales, [bh][nq_blocks]
+  const float* ksc;      // k scales, [bh][nk_pad / 64]
+  int32_t nq_blocks;
+  int32_t nk_blocks;
   int32_t kv_len[kMaxBatch];  // valid keys of each entry
+};
+
+struct QuantArgs {
+  const __bf16* q;       // q of head `head_begin`, token 0, entry 0
+  const __bf16* k;
+  int64_t q_row, k_row;  // elements between consecutive tokens
+  int64_t q_batch, k_batch;
+  int64_t head;          // elements between consecutive heads (= d)
+  int8_t* qc;
+  int8_t* kc;
+  int64_t qc_bh, kc_bh;
+  float* qsc;
+  float* ksc;
+  int32_t nq;
+  int32_t nq_blocks;     // ceil(nq / 128)
+  int32_t nk_blocks;     // blocks of the workspace (nk_pad / 64)
+  int32_t hc;
+  int32_t batch;
+  float sm_scale;        // multiplies q before quantization
+  int32_t kv_len[kMaxBatch];
 };
 
 struct PrepArgs {
@@ -129,8 +175,9 @@ struct PrepArgs {
 };
 
 // Host-side launchers (defined in the kernel translation units).
-hipError_t launch_attn_fwd(const AttnArgs& a, int head_dim, bool rope_q, hipStream_t s);
+hipError_t launch_attn_fwd(const AttnArgs& a, int head_dim, bool rope_q, bool qk_int8, hipStream_t s);
 hipError_t launch_prepare(const PrepArgs& a, int head_dim, bool rope_k, hipStream_t s);
+hipError_t launch_quantize(const QuantArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_pack(const void* src, void* dst, int64_t n, int32_t ht, int32_t d, int32_t groups,
                        bool unpack, hipStream_t s);
 hipError_t launch_rope_probe(const RopeGeom& g, int32_t nq, int32_t head_dim, int32_t* out, hipStream_t s);

@@ -78,6 +78,73 @@ __global__ void __launch_bounds__(256) prepare_kernel(PrepArgs a) {
   }
 }
 
+// Symmetric int8 codes of one block of consecutive tokens of one (entry, head):
+// blockIdx.z = 0 quantizes q, multiplied by the softmax scale, in blocks of 128
+// tokens; blockIdx.z = 1 quantizes k in blocks of 64 valid keys. Each decision is
+// float32, in this order: x = float(bf16) (* softmax scale for q); amax = max |x|
+// over the block; scale = amax / 127 (IEEE division), replaced by 1 below 2^-100;
+// code = rint(x / scale) (IEEE division, ties to even), clamped to [-127, 127].
+template <int D>
+__global__ void __launch_bounds__(256) quantize_kernel(QuantArgs a) {
+  constexpr int kChunks = D / 8;                   // 8-element chunks per token
+  constexpr int kPer = kQuantQ * kChunks / 256;    // chunks per thread, q blocks
+  __shared__ float red[4];
+  const bool is_q = blockIdx.z == 0;
+  const int blk = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int bat = bh / a.hc;
+  const int head = bh - bat * a.hc;
+  const int n = is_q ? a.nq : a.kv_len[bat];
+  const int per_block = is_q ? kQuantQ : kQuantK;
+  if (blk * per_block >= n) return;                // whole workgroup
+  const int r0 = blk * per_block;
+  const int total = min(per_block, n - r0) * kChunks;
+  const __bf16* src = is_q ? a.q + bat * a.q_batch + (int64_t)head * a.head
+                           : a.k + bat * a.k_batch + (int64_t)head * a.head;
+  const int64_t row = is_q ? a.q_row : a.k_row;
+  const int tid = threadIdx.x;
+
+  float x[kPer][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int c = i * 256 + tid;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[i][e] = 0.0f;
+    if (c < total) {
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(src + (int64_t)(r0 + c / kChunks) * row + (c % kChunks) * 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x[i][e] = is_q ? (float)v[e] * a.sm_scale : (float)v[e];
+        amax = fmaxf(amax, fabsf(x[i][e]));
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float scale = __fdiv_rn(amax, 127.0f);
+  if (!(scale >= 0x1p-100f)) scale = 1.0f;
+  if (tid == 0) (is_q ? a.qsc + (int64_t)bh * a.nq_blocks : a.ksc + (int64_t)bh * a.nk_blocks)[blk] = scale;
+
+  int8_t* dst = (is_q ? a.qc + bh * a.qc_bh : a.kc + bh * a.kc_bh) + (int64_t)r0 * D;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int c = i * 256 + tid;
+    if (c < total) {
+      uint32_t w[2] = {0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float qv = fminf(fmaxf(__builtin_rintf(__fdiv_rn(x[i][e], scale)), -127.0f), 127.0f);
+        w[e >> 2] |= (uint32_t)(uint8_t)(int8_t)(int)qv << (8 * (e & 3));
+      }
+      *reinterpret_cast<uint2*>(dst + (int64_t)c * 8) = make_uint2(w[0], w[1]);
+    }
+  }
+}
+
 // One workgroup per token row: moves that token's Ht * d elements between the
 // [n, Ht, d] and [G, n, Ht/G, d] layouts in 16-byte chunks.
 __global__ void __launch_bounds__(256) pack_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
@@ -122,6 +189,14 @@ hipError_t launch_prepare(const PrepArgs& a, int head_dim, bool rope_k, hipStrea
   if (head_dim == 128) return rope_k ? launch_prepare_t<128, true>(a, s) : launch_prepare_t<128, false>(a, s);
   if (head_dim == 64) return rope_k ? launch_prepare_t<64, true>(a, s) : launch_prepare_t<64, false>(a, s);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_quantize(const QuantArgs& a, int head_dim, hipStream_t s) {
+  if (head_dim != 128 || a.hc <= 0 || a.batch <= 0 || a.batch > kMaxBatch || (int64_t)a.hc * a.batch > 65535)
+    return hipErrorInvalidValue;
+  const int nblk = a.nq_blocks > a.nk_blocks ? a.nq_blocks : a.nk_blocks;
+  hipLaunchKernelGGL(quantize_kernel<128>, dim3(nblk, a.hc * a.batch, 2), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_pack(const void* src, void* dst, int64_t n, int32_t ht, int32_t d, int32_t groups,

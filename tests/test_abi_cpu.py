@@ -108,6 +108,9 @@ ROPE = {"grid": (4, 32, 32), "dims": (44, 42, 42), "base": 10000.0}
     (dict(batch=-1), INVALID),
     (dict(batch=65), UNSUPPORTED),
     (dict(batch=64, head_count=1025, heads_total=2048), UNSUPPORTED),
+    (dict(qk_int8=True, head_dim=64), UNSUPPORTED),
+    (dict(qk_int8=True, rope=ROPE), UNSUPPORTED),
+    (dict(qk_int8=True, nq=64, nk=262145), UNSUPPORTED),
 ])
 def test_create_rejects_bad_descriptors(lib, kw, code):
     st, h = vd.create_raw(_desc(**kw))
