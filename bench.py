@@ -10,7 +10,9 @@ Prints one JSON line. ``value`` = 4 * N * N * d * H / step time (TFLOP/s).
 ``kernels`` adds, outside the timed steps, pack/unpack bandwidth and two batched
 calls (two sequences per call, as under classifier-free guidance): the same
 self-attention with B = 2, and text cross-attention over all 40 heads with key
-lengths 512 and 226.
+lengths 512 and 226; and the same workload with q.k on int8 per-block codes
+(``qk_int8_*``: nominal TFLOP/s, and the fraction of a roofline that prices q.k
+at the int8 MFMA peak and the weighted sum at the float16 peak).
 ``roofline`` prices the attention kernel alone against the MI355X dense
 bf16/fp16 MFMA peak, with its duration from HIP events on the launch stream.
 ``cpu_baseline`` times the float64 oracle on a bounded sample of query rows.
@@ -34,6 +36,7 @@ HEADS_TOTAL, HEAD_BEGIN, HEAD_COUNT, D = 40, 0, 10, 128
 SEED = 1003
 PEAK_TFLOPS = 2500.0          # MI355X dense bf16 / fp16 MFMA
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+PEAK_INT8_TOPS = 5000.0       # MI355X dense int8 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_n75600_h10_traffic.json")
 KERNEL_SOURCES = ["long_sequence_attention_amd/csrc/attn_fwd.hip", "long_sequence_attention_amd/csrc/common.hpp"]
 
@@ -191,6 +194,20 @@ def main() -> int:
     batched["batch2_cross_ms"] = round(ms, 3)
     batched["batch2_cross_TFLOPs"] = round(4.0 * N_TOK * sum(lens) * D * HEADS_TOTAL / (ms * 1e-3) / 1e12, 1)
     del bq, xk, xv, wsx, ox, ax
+
+    # q.k on int8 per-block codes at the workload's shape. Its roofline prices the
+    # q.k half at the int8 MFMA peak and the weighted sum at the float16 one.
+    a8 = vd.Attention(N_TOK, N_TOK, HEADS_TOTAL, D, head_begin=HEAD_BEGIN, head_count=HEAD_COUNT, qk_int8=True)
+    ws8 = a8.new_workspace(dev)
+    o8 = torch.empty(a8.out_shape, dtype=torch.bfloat16, device=dev)
+    prep8 = time_calls(lambda: a8.prepare(qd, kd, vdd, workspace=ws8), 3)
+    att8 = time_calls(lambda: a8.attend(qd, kd, vdd, out=o8, workspace=ws8), 3)
+    t_peak8 = (flops / 2) / (PEAK_INT8_TOPS * 1e12) + (flops / 2) / (PEAK_TFLOPS * 1e12)
+    batched["qk_int8_prepare_ms"] = round(prep8, 4)
+    batched["qk_int8_attend_ms"] = round(att8, 3)
+    batched["qk_int8_TFLOPs"] = round(flops / (att8 * 1e-3) / 1e12, 1)
+    batched["qk_int8_roofline_frac"] = round(t_peak8 / (att8 * 1e-3), 4)
+    del a8, ws8, o8
 
     result = {
         "metric": "attention TFLOP/s + % bf16 MFMA peak at N=75600,H=10,d=128 (1 GPU)",
