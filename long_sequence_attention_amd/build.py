@@ -2,8 +2,10 @@
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -30,17 +32,52 @@ def hipcc() -> str:
     return path if os.path.exists(path) else "hipcc"
 
 
+# Kernels whose registers must never spill to scratch memory: an outlined helper
+# or a spill moves their score and accumulator arrays into scratch and costs an
+# order of magnitude, with correct results, so the build rejects it.
+NO_SCRATCH_SOURCES = ["attn_fwd.hip", "prepass.hip"]
+
+
+def _scratch_users(asm: str) -> list[str]:
+    """Kernels whose code-object metadata asks for private (scratch) memory."""
+    users = []
+    for block in asm.split("\n  - ")[1:]:
+        name = re.search(r"\.name:\s+(\S+)", block)
+        size = re.search(r"\.private_segment_fixed_size:\s+(\d+)", block)
+        if name and size and int(size.group(1)) > 0:
+            users.append(f"{name.group(1)} ({size.group(1)} bytes per lane)")
+    return users
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source into the shared library; returns its path."""
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     tmp = LIB + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", *srcs, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed ({res.returncode}) building {LIB}")
+    with tempfile.TemporaryDirectory() as td:
+        # device assembly of the hot kernels, compiled alongside, for the scratch check
+        checks = []
+        for name in NO_SCRATCH_SOURCES:
+            asm = os.path.join(td, name + ".s")
+            flags = [f for f in HIPCC_FLAGS if f not in ("-fPIC", "-shared")]
+            acmd = [hipcc(), *flags, "--cuda-device-only", "-S", f"-I{INCLUDE}", f"-I{CSRC}",
+                    os.path.join(CSRC, name), "-o", asm]
+            checks.append((asm, subprocess.Popen(acmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            sys.stderr.write(res.stdout + res.stderr)
+            raise RuntimeError(f"hipcc failed ({res.returncode}) building {LIB}")
+        for asm, proc in checks:
+            out, err = proc.communicate()
+            if proc.returncode != 0:
+                sys.stderr.write(out + err)
+                raise RuntimeError(f"hipcc failed ({proc.returncode}) compiling {asm} for the scratch check")
+            with open(asm) as f:
+                users = _scratch_users(f.read())
+            if users:
+                raise RuntimeError("kernels use scratch memory (spills or outlined helpers): " + "; ".join(users))
     os.replace(tmp, LIB)
     return LIB
 
