@@ -22,6 +22,9 @@ Everything here is plain float64 numpy, written from the definitions:
   * ``int8_qk``: attention on q and k quantized to int8 per block (the
     ``per_block_int8`` step of SageAttention in the same ComfyUI traceback), with
     every code decided in float32 as the library decides it.
+  * ``vsa``: block-sparse attention over 64-token tiles (the VSA kernels run at
+    sparsity 0.8 with 64-token tiles on FastVideo's "Pair two NVIDIA DGX Sparks"
+    page), with the tile selection decided in float32 as the library decides it.
 
 Parity status of each function is stated in its docstring.
 """
@@ -39,4 +42,9 @@ from .attention import (  # noqa: F401
 from .int8_qk import (  # noqa: F401
     quantize_blocks,
     mha_reference_qk_int8,
+)
+from .vsa import (  # noqa: F401
+    keep_count as vsa_keep_count,
+    vsa_select,
+    vsa_reference,
 )
