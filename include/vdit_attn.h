@@ -251,6 +251,74 @@ vdit_status_t vdit_unpack_heads(const void* src, void* dst, int32_t n, int32_t h
  */
 vdit_status_t vdit_attn_rope_probe(vdit_attn_t h, int32_t* idx_out, void* hip_stream);
 
+/*
+ * Block-sparse attention over 64-token tiles (video sparse attention). FastVideo
+ * "Pair two NVIDIA DGX Sparks": section "3. Generate one FastH3 clip on both
+ * GPUs" names the VSA attention kernels, and section "Released V2, FastH3-QAD-v2
+ * and Trim NVFP4 stacks" runs them at sparsity 0.8 with 64-token tiles. Nothing
+ * more is stated; the reading implemented (that of the published video sparse
+ * attention method, without its learned gates and coarse output branch) is:
+ *
+ *   tiles      runs of 64 consecutive tokens as the tensors hold them (the last
+ *              one shorter if n is not a multiple of 64); Tq = ceil(nq/64) query
+ *              tiles, Tk = ceil(nk/64) key tiles. A caller that wants tiles to
+ *              be 4x4x4 cubes of the latent grid orders the tokens that way first.
+ *   coarse     mean of each tile of q and of k (float32 sum in token order, then
+ *              divided by the tile's token count); score(i, j) = sum over c of
+ *              mean_q(i)[c] * mean_k(j)[c], each product and partial sum rounded
+ *              to float32, c ascending (the positive softmax scale ranks nothing
+ *              differently and is left out).
+ *   selection  query tile i keeps the `keep` key tiles of highest score; equal
+ *              scores keep the lower tile index; -0 equals +0 and NaN ranks
+ *              lowest. keep = ceil((1 - sparsity) * Tk), at least 1.
+ *   fine       every query of tile i attends over the keys of its kept tiles
+ *              only, with the numerics of vdit_attn_fwd (fixed-reference softmax
+ *              taken over the first kept tile).
+ *
+ * A plan for these calls has no key mask, no RoPE and no qk_int8 (UNSUPPORTED
+ * otherwise); batch, both layouts and d = 64 or 128 work as for vdit_attn_fwd.
+ * Limits: Tk <= 8192 and keep <= 4096 (UNSUPPORTED beyond); 1 <= keep <= Tk
+ * (INVALID_ARG otherwise).
+ *
+ * vdit_vsa_keep: keep for a sparsity in [0, 1) (INVALID_ARG otherwise). Host only.
+ * vdit_vsa_workspace_bytes: workspace bytes that every vsa call accepts for this
+ *   keep: the attention workspace (v transposed), then the kept tiles
+ *   (int32 [B][head_count][Tq][keep]), the tile means (float32 [B][head_count][Tq][d]
+ *   and [B][head_count][Tk][d]) and the coarse scores (float32
+ *   [B][head_count][Tq][Tk]), each region 256-byte aligned. Host only.
+ */
+vdit_status_t vdit_vsa_keep(vdit_attn_t h, double sparsity, int32_t* keep);
+vdit_status_t vdit_vsa_workspace_bytes(vdit_attn_t h, int32_t keep, size_t* bytes);
+
+/*
+ * Coarse stage: writes the kept key tiles of every (entry, head, query tile),
+ * ascending, to `tiles` (device int32 [B][head_count][Tq][keep], 4-byte aligned).
+ * q, k as for vdit_attn_fwd (N3HD: the packed tensor in q, k NULL); v is not
+ * needed. workspace >= vdit_vsa_workspace_bytes(keep); `tiles` must not overlap
+ * the inputs or the workspace (INVALID_ARG).
+ */
+vdit_status_t vdit_vsa_select(vdit_attn_t h, const void* q, const void* k, int32_t keep, int32_t* tiles,
+                              void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * Fine stage with caller-given tiles (device int32 [B][head_count][Tq][keep], e.g.
+ * from vdit_vsa_select): prepares v into the workspace (>= vdit_attn_workspace_bytes)
+ * and runs the block-sparse attention. A tile index outside [0, Tk) is clamped
+ * into it (memory stays in bounds; the result then attends over the clamped
+ * tile); listing a tile twice counts its keys twice. `tiles` must not overlap
+ * out or the workspace. Other arguments as for vdit_attn_fwd.
+ */
+vdit_status_t vdit_vsa_attend(vdit_attn_t h, const void* q, const void* k, const void* v, int32_t keep,
+                              const int32_t* tiles, void* out, void* workspace, size_t workspace_bytes,
+                              void* hip_stream);
+
+/*
+ * Both stages: vdit_vsa_select into the workspace, then vdit_vsa_attend.
+ * workspace >= vdit_vsa_workspace_bytes(keep). Other arguments as for vdit_attn_fwd.
+ */
+vdit_status_t vdit_vsa_fwd(vdit_attn_t h, const void* q, const void* k, const void* v, int32_t keep, void* out,
+                           void* workspace, size_t workspace_bytes, void* hip_stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* vdit_status_string(vdit_status_t s);
 

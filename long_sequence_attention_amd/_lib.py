@@ -47,6 +47,11 @@ SIGNATURES = {
     "vdit_pack_heads": (_ST, [_P, _P, _I, _I, _I, _I, _P]),
     "vdit_unpack_heads": (_ST, [_P, _P, _I, _I, _I, _I, _P]),
     "vdit_attn_rope_probe": (_ST, [_P, _P, _P]),
+    "vdit_vsa_keep": (_ST, [_P, ctypes.c_double, ctypes.POINTER(_I)]),
+    "vdit_vsa_workspace_bytes": (_ST, [_P, _I, ctypes.POINTER(_S)]),
+    "vdit_vsa_select": (_ST, [_P, _P, _P, _I, _P, _P, _S, _P]),
+    "vdit_vsa_attend": (_ST, [_P, _P, _P, _P, _I, _P, _P, _P, _S, _P]),
+    "vdit_vsa_fwd": (_ST, [_P, _P, _P, _P, _I, _P, _P, _S, _P]),
     "vdit_status_string": (ctypes.c_char_p, [_ST]),
 }
 

@@ -202,6 +202,88 @@ class Attention:
                                                    _ptr(workspace), nbytes, sp), "vdit_attn_attend_lens")
         return out
 
+    # -- block-sparse attention over 64-token tiles (vdit_vsa_*)
+    @property
+    def q_tiles(self) -> int:
+        return (self.desc.nq + 63) // 64
+
+    @property
+    def k_tiles(self) -> int:
+        return (self.desc.nk + 63) // 64
+
+    def vsa_keep(self, sparsity: float) -> int:
+        """Key tiles kept per query tile at ``sparsity``: ceil((1 - sparsity) * Tk), >= 1."""
+        k = ctypes.c_int32()
+        _check(self._lib.vdit_vsa_keep(self._h, float(sparsity), ctypes.byref(k)), "vdit_vsa_keep")
+        return int(k.value)
+
+    def vsa_workspace_bytes(self, keep: int) -> int:
+        n = ctypes.c_size_t()
+        _check(self._lib.vdit_vsa_workspace_bytes(self._h, int(keep), ctypes.byref(n)), "vdit_vsa_workspace_bytes")
+        return int(n.value)
+
+    def new_vsa_workspace(self, keep: int, device) -> torch.Tensor:
+        return torch.empty(max(self.vsa_workspace_bytes(keep), 16), dtype=torch.uint8, device=device)
+
+    def tiles_shape(self, keep: int):
+        return self._lead() + (self.desc.head_count, self.q_tiles, int(keep))
+
+    def _keep(self, keep, sparsity):
+        if (keep is None) == (sparsity is None):
+            raise ValueError("give exactly one of keep and sparsity")
+        return int(keep) if keep is not None else self.vsa_keep(sparsity)
+
+    def vsa_select(self, q, k=None, *, keep: int | None = None, sparsity: float | None = None, tiles=None,
+                   workspace=None, stream=None) -> torch.Tensor:
+        """Kept key tiles, int32 [B?, head_count, Tq, keep], ascending per query tile."""
+        keep = self._keep(keep, sparsity)
+        d = self.desc
+        b = self._lead()
+        if self.layout == "N3HD":
+            _need(q, b + (d.nq, 3, d.heads_total, d.head_dim), torch.bfloat16, "qkv")
+            if k is not None:
+                raise ValueError("the packed layout takes the [N, 3, H, d] tensor alone")
+        else:
+            _need(q, b + (d.nq, d.heads_total, d.head_dim), torch.bfloat16, "q")
+            _need(k, b + (d.nk, d.heads_total, d.head_dim), torch.bfloat16, "k")
+        if tiles is None:
+            tiles = torch.empty(self.tiles_shape(keep), dtype=torch.int32, device=q.device)
+        _need(tiles, self.tiles_shape(keep), torch.int32, "tiles")
+        if workspace is None:
+            workspace = self.new_vsa_workspace(keep, q.device)
+        _check(self._lib.vdit_vsa_select(self._h, _ptr(q), _ptr(k), keep, _ptr(tiles), _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(), _stream_ptr(q, stream)),
+               "vdit_vsa_select")
+        return tiles
+
+    def vsa_attend(self, q, k=None, v=None, *, tiles, out=None, workspace=None, stream=None) -> torch.Tensor:
+        """Block-sparse attention over the key tiles in ``tiles`` [B?, head_count, Tq, keep]."""
+        self._check_inputs(q, k, v)
+        keep = int(tiles.shape[-1]) if isinstance(tiles, torch.Tensor) else 0
+        _need(tiles, self.tiles_shape(keep), torch.int32, "tiles")
+        if out is None:
+            out = torch.empty(self.out_shape, dtype=torch.bfloat16, device=q.device)
+        _need(out, self.out_shape, torch.bfloat16, "out")
+        ws = self._ws(workspace, q.device)
+        _check(self._lib.vdit_vsa_attend(self._h, _ptr(q), _ptr(k), _ptr(v), keep, _ptr(tiles), _ptr(out), _ptr(ws),
+                                         ws.numel() * ws.element_size(), _stream_ptr(q, stream)), "vdit_vsa_attend")
+        return out
+
+    def vsa_forward(self, q, k=None, v=None, *, keep: int | None = None, sparsity: float | None = None, out=None,
+                    workspace=None, stream=None) -> torch.Tensor:
+        """Coarse selection then block-sparse attention (vdit_vsa_fwd)."""
+        keep = self._keep(keep, sparsity)
+        self._check_inputs(q, k, v)
+        if out is None:
+            out = torch.empty(self.out_shape, dtype=torch.bfloat16, device=q.device)
+        _need(out, self.out_shape, torch.bfloat16, "out")
+        if workspace is None:
+            workspace = self.new_vsa_workspace(keep, q.device)
+        _check(self._lib.vdit_vsa_fwd(self._h, _ptr(q), _ptr(k), _ptr(v), keep, _ptr(out), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(), _stream_ptr(q, stream)),
+               "vdit_vsa_fwd")
+        return out
+
     def rope_probe(self, device, stream=None) -> torch.Tensor:
         d = self.desc
         out = torch.empty((d.nq, d.head_dim // 2, 5), dtype=torch.int32, device=device)

@@ -490,6 +490,209 @@ vdit_status_t vdit_attn_rope_probe(vdit_attn_t h, int32_t* idx_out, void* hip_st
   return VDIT_OK;
 }
 
+}  // extern "C"
+
+// ---- block-sparse attention over 64-token tiles
+namespace {
+
+struct VsaLayout {
+  int32_t tq, tk;
+  size_t tiles_off, qm_off, km_off, s_off, total;
+};
+
+int32_t tiles_of(int32_t n) { return (n + vdit::kBlockN - 1) / vdit::kBlockN; }
+
+// Workspace: the attention part (transposed v), then the kept tiles (vdit_vsa_fwd),
+// the tile means of q and k and the coarse scores, each 256-byte aligned.
+VsaLayout vsa_layout(const vdit_attn& h, int32_t keep) {
+  const vdit_attn_desc_t& d = h.desc;
+  VsaLayout l{};
+  l.tq = tiles_of(d.nq);
+  l.tk = tiles_of(d.nk);
+  const size_t bh = (size_t)d.batch * d.head_count;
+  l.tiles_off = align_up(h.ws_total, 256);
+  l.qm_off = align_up(l.tiles_off + bh * l.tq * (size_t)keep * sizeof(int32_t), 256);
+  l.km_off = align_up(l.qm_off + bh * l.tq * (size_t)d.head_dim * sizeof(float), 256);
+  l.s_off = align_up(l.km_off + bh * l.tk * (size_t)d.head_dim * sizeof(float), 256);
+  l.total = l.s_off + bh * l.tq * (size_t)l.tk * sizeof(float);
+  return l;
+}
+
+vdit_status_t vsa_check(const vdit_attn* h, int32_t keep) {
+  if (!is_live(h)) return VDIT_ERR_INVALID_ARG;
+  const vdit_attn_desc_t& d = h->desc;
+  if (d.use_key_mask || d.use_rope || d.qk_int8) return VDIT_ERR_UNSUPPORTED;
+  const int32_t tk = tiles_of(d.nk);
+  if (tk > vdit::kVsaMaxTiles) return VDIT_ERR_UNSUPPORTED;
+  if (keep < 1 || keep > tk) return VDIT_ERR_INVALID_ARG;
+  if (keep > vdit::kVsaMaxKeep) return VDIT_ERR_UNSUPPORTED;
+  return VDIT_OK;
+}
+
+vdit_status_t vsa_call_checks(const vdit_attn& h, const VsaLayout& l, void* ws, size_t ws_bytes) {
+  if (!ws || ws_bytes < l.total) return VDIT_ERR_WORKSPACE;
+  if (!aligned16(ws)) return VDIT_ERR_ALIGNMENT;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != h.device) return VDIT_ERR_DEVICE;
+  return VDIT_OK;
+}
+
+bool ws_overlaps_inputs(const Inputs& in, const void* p, size_t n) {
+  return overlaps(p, n, in.q_base, in.q_bytes) || overlaps(p, n, in.k_base, in.k_bytes) ||
+         overlaps(p, n, in.v_base, in.v_bytes);
+}
+
+vdit_status_t do_vsa_select(const vdit_attn& h, const Inputs& in, const VsaLayout& l, int32_t keep,
+                            int32_t* tiles, void* ws, hipStream_t s) {
+  const vdit_attn_desc_t& d = h.desc;
+  char* w = static_cast<char*>(ws);
+  const int32_t bh = d.batch * d.head_count;
+  vdit::VsaMeanArgs m{};
+  m.hc = d.head_count;
+  m.bh = bh;
+  m.x = in.q;
+  m.row = in.q_row;
+  m.batch = in.q_batch;
+  m.mean = reinterpret_cast<float*>(w + l.qm_off);
+  m.n = d.nq;
+  m.tiles = l.tq;
+  if (vdit::launch_vsa_means(m, d.head_dim, s) != hipSuccess) return VDIT_ERR_DEVICE;
+  m.x = in.k;
+  m.row = in.kv_row;
+  m.batch = in.kv_batch;
+  m.mean = reinterpret_cast<float*>(w + l.km_off);
+  m.n = d.nk;
+  m.tiles = l.tk;
+  if (vdit::launch_vsa_means(m, d.head_dim, s) != hipSuccess) return VDIT_ERR_DEVICE;
+  vdit::VsaSelectArgs a{};
+  a.qm = reinterpret_cast<const float*>(w + l.qm_off);
+  a.km = reinterpret_cast<const float*>(w + l.km_off);
+  a.s = reinterpret_cast<float*>(w + l.s_off);
+  a.tiles = tiles;
+  a.tq = l.tq;
+  a.tk = l.tk;
+  a.keep = keep;
+  a.d = d.head_dim;
+  a.bh = bh;
+  if (vdit::launch_vsa_select(a, s) != hipSuccess) return VDIT_ERR_DEVICE;
+  return VDIT_OK;
+}
+
+vdit_status_t do_vsa_attend(const vdit_attn& h, const Inputs& in, int32_t keep, const int32_t* tiles, void* out,
+                            void* ws, hipStream_t s) {
+  const vdit_attn_desc_t& d = h.desc;
+  KeyLens kl;
+  vdit_status_t st = resolve_lens(h, false, 0, nullptr, kl);
+  if (st != VDIT_OK) return st;
+  if ((st = do_prepare(h, in, kl, ws, s)) != VDIT_OK) return st;
+  vdit::AttnArgs a{};
+  a.q = in.q;
+  a.q_row = in.q_row;
+  a.q_head = d.head_dim;
+  a.q_batch = in.q_batch;
+  a.k = in.k;
+  a.k_row = in.kv_row;
+  a.k_head = d.head_dim;
+  a.k_batch = in.kv_batch;
+  a.vt = reinterpret_cast<const _Float16*>(static_cast<const char*>(ws) + h.ws_vt_off);
+  a.vt_head = h.nk_pad * d.head_dim;
+  a.vt_batch = a.vt_head * d.head_count;
+  a.out = static_cast<__bf16*>(out);
+  a.out_batch = (int64_t)d.nq * d.head_count * d.head_dim;
+  a.nq = d.nq;
+  a.hc = d.head_count;
+  a.batch = d.batch;
+  a.c = h.c;
+  a.tiles = tiles;
+  a.keep = keep;
+  for (int32_t b = 0; b < vdit::kMaxBatch; ++b) a.kv_len[b] = kl.len[b];
+  if (vdit::launch_attn_sparse(a, d.head_dim, s) != hipSuccess) return VDIT_ERR_DEVICE;
+  return VDIT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+vdit_status_t vdit_vsa_keep(vdit_attn_t h, double sparsity, int32_t* keep) {
+  if (!is_live(h) || !keep) return VDIT_ERR_INVALID_ARG;
+  if (!(sparsity >= 0.0 && sparsity < 1.0)) return VDIT_ERR_INVALID_ARG;
+  const int32_t tk = tiles_of(h->desc.nk);
+  const double want = std::ceil((1.0 - sparsity) * (double)tk);
+  *keep = want < 1.0 ? 1 : (want > (double)tk ? tk : (int32_t)want);
+  return VDIT_OK;
+}
+
+vdit_status_t vdit_vsa_workspace_bytes(vdit_attn_t h, int32_t keep, size_t* bytes) {
+  if (!bytes) return VDIT_ERR_INVALID_ARG;
+  const vdit_status_t st = vsa_check(h, keep);
+  if (st != VDIT_OK) return st;
+  *bytes = vsa_layout(*h, keep).total;
+  return VDIT_OK;
+}
+
+vdit_status_t vdit_vsa_select(vdit_attn_t h, const void* q, const void* k, int32_t keep, int32_t* tiles,
+                              void* workspace, size_t workspace_bytes, void* hip_stream) {
+  vdit_status_t st = vsa_check(h, keep);
+  if (st != VDIT_OK) return st;
+  Inputs in{};
+  // the packed layout carries k inside q; with separate tensors v is not read
+  const void* v = h->desc.layout == VDIT_LAYOUT_N3HD ? nullptr : k;
+  if ((st = resolve_inputs(*h, q, k, v, in)) != VDIT_OK) return st;
+  if (!tiles) return VDIT_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(tiles) & 3u) return VDIT_ERR_ALIGNMENT;
+  const VsaLayout l = vsa_layout(*h, keep);
+  if ((st = vsa_call_checks(*h, l, workspace, workspace_bytes)) != VDIT_OK) return st;
+  const size_t tb = (size_t)h->desc.batch * h->desc.head_count * l.tq * keep * sizeof(int32_t);
+  if (ws_overlaps_inputs(in, workspace, l.total) || ws_overlaps_inputs(in, tiles, tb) ||
+      overlaps(tiles, tb, workspace, l.total))
+    return VDIT_ERR_INVALID_ARG;
+  return do_vsa_select(*h, in, l, keep, tiles, workspace, static_cast<hipStream_t>(hip_stream));
+}
+
+vdit_status_t vdit_vsa_attend(vdit_attn_t h, const void* q, const void* k, const void* v, int32_t keep,
+                              const int32_t* tiles, void* out, void* workspace, size_t workspace_bytes,
+                              void* hip_stream) {
+  vdit_status_t st = vsa_check(h, keep);
+  if (st != VDIT_OK) return st;
+  Inputs in{};
+  if ((st = resolve_inputs(*h, q, k, v, in)) != VDIT_OK) return st;
+  if ((st = check_out(*h, in, out, workspace)) != VDIT_OK) return st;
+  if (!tiles) return VDIT_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(tiles) & 3u) return VDIT_ERR_ALIGNMENT;
+  // the attention part of the workspace is all this call writes besides out
+  if (!workspace || workspace_bytes < h->ws_total) return VDIT_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return VDIT_ERR_ALIGNMENT;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != h->device) return VDIT_ERR_DEVICE;
+  const size_t tb = (size_t)h->desc.batch * h->desc.head_count * tiles_of(h->desc.nq) * keep * sizeof(int32_t);
+  const size_t ob = (size_t)h->desc.batch * h->desc.nq * h->desc.head_count * h->desc.head_dim * 2;
+  if (ws_overlaps_inputs(in, workspace, h->ws_total) || overlaps(tiles, tb, workspace, h->ws_total) ||
+      overlaps(tiles, tb, out, ob))
+    return VDIT_ERR_INVALID_ARG;
+  return do_vsa_attend(*h, in, keep, tiles, out, workspace, static_cast<hipStream_t>(hip_stream));
+}
+
+vdit_status_t vdit_vsa_fwd(vdit_attn_t h, const void* q, const void* k, const void* v, int32_t keep, void* out,
+                           void* workspace, size_t workspace_bytes, void* hip_stream) {
+  vdit_status_t st = vsa_check(h, keep);
+  if (st != VDIT_OK) return st;
+  Inputs in{};
+  if ((st = resolve_inputs(*h, q, k, v, in)) != VDIT_OK) return st;
+  const VsaLayout l = vsa_layout(*h, keep);
+  if ((st = vsa_call_checks(*h, l, workspace, workspace_bytes)) != VDIT_OK) return st;
+  const size_t ob = (size_t)h->desc.batch * h->desc.nq * h->desc.head_count * h->desc.head_dim * 2;
+  if (!out) return VDIT_ERR_INVALID_ARG;
+  if (!aligned16(out)) return VDIT_ERR_ALIGNMENT;
+  if (ws_overlaps_inputs(in, workspace, l.total) || ws_overlaps_inputs(in, out, ob) ||
+      overlaps(out, ob, workspace, l.total))
+    return VDIT_ERR_INVALID_ARG;
+  const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  int32_t* tiles = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + l.tiles_off);
+  if ((st = do_vsa_select(*h, in, l, keep, tiles, workspace, s)) != VDIT_OK) return st;
+  return do_vsa_attend(*h, in, keep, tiles, out, workspace, s);
+}
+
 const char* vdit_status_string(vdit_status_t s) {
   switch (s) {
     case VDIT_OK: return "VDIT_OK";

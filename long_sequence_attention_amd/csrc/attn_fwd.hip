@@ -21,6 +21,10 @@
 // SIMD are kept half an iteration apart (one forms scores and weights while the
 // other runs products), so the SIMD's matrix and vector units overlap.
 //
+// Block-sparse mode (SPARSE): the workgroup is one 64-query tile (two waves) and
+// visits only the key tiles listed for it, in list order; everything else is the
+// same per wave.
+//
 // Softmax: the weights use a fixed reference, the row maximum of the first key
 // tile, in the log2 domain (c = scale * log2 e): p = 2^(s*c - m). O is never
 // rescaled. If some later score exceeds the reference by more than the float16
@@ -94,11 +98,12 @@ struct FwdCfg {
 // the next tile are converted to float during the weight products; each tile's
 // weights then use c = q scale * k scale * log2 e per lane, so the softmax costs
 // one conversion per score more than with bfloat16 q.k.
-template <int D, int QB, int WAVES, int NST, bool ROPE, bool QK8>
+template <int D, int QB, int WAVES, int NST, bool ROPE, bool QK8, bool SPARSE>
 __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   using C = FwdCfg<D, QB, WAVES, QK8>;
   using QFrag = typename std::conditional<QK8, i32x4, bf16x8>::type;
   static_assert(!(QK8 && ROPE), "int8 q.k takes no RoPE");
+  static_assert(!SPARSE || (!QK8 && !ROPE && C::kBlockM == 64), "block-sparse: bfloat16, 64-query tiles");
   static_assert(NST == 4 || NST == 2, "stage count");
   static_assert(NST == 2 || WAVES % 2 == 0, "the wave offset pairs waves w and w + WAVES/2");
   // K and V^T stages, each its own array (not one array indexed by stage) so
@@ -117,6 +122,8 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   __shared__ int wg_retry;
   // int8 q.k: k scale of every key tile of this (entry, head), copied in the prologue
   __shared__ float ks_lds[QK8 ? (NST == 4 ? kQK8MaxTiles : kSmallKeys / kBlockN) : 1];
+  // block-sparse: the key tiles this workgroup visits
+  __shared__ uint16_t tile_lds[SPARSE ? kVsaMaxKeep : 1];
 
   // Workgroups are dispatched round-robin over the 8 XCDs; renumber them so that
   // each XCD walks a contiguous range of (head, query tile) and its L2 serves the
@@ -173,7 +180,22 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   }
 
   const int kv_len = a.kv_len[bat];
-  const int ntiles = (kv_len + kBlockN - 1) / kBlockN;
+  const int ktiles = (kv_len + kBlockN - 1) / kBlockN;  // key tiles of the entry
+  const int ntiles = SPARSE ? a.keep : ktiles;           // key tiles visited
+  if constexpr (SPARSE) {
+    // tile indices out of range are clamped, so every load stays in bounds
+    const int32_t* lst = a.tiles + ((int64_t)bh * a.n_qtiles + qtile) * a.keep;
+    for (int i = tid; i < ntiles; i += C::kThreads) tile_lds[i] = (uint16_t)min(max(lst[i], 0), ktiles - 1);
+    __syncthreads();
+  }
+  // key tile of visit t; visits past the last one repeat it
+  auto tile_of = [&](int t) -> int {
+    t = min(t, ntiles - 1);
+    if constexpr (SPARSE)
+      return tile_lds[t];
+    else
+      return t;
+  };
   const char* kbytes = QK8 ? reinterpret_cast<const char*>(a.kc + bh * a.kc_bh)
                            : reinterpret_cast<const char*>(a.k + bat * a.k_batch + (int64_t)head * a.k_head);
   const char* vbytes = reinterpret_cast<const char*>(a.vt + bat * a.vt_batch + (int64_t)head * a.vt_head);
@@ -216,7 +238,7 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   // no row at or beyond kv_len is ever read; tiles past the last one re-read it.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   auto dma_k = [&](int t, const char* st) {
-    t = min(t, ntiles - 1);
+    t = tile_of(t);
     const char* kt = kbytes + (int64_t)t * kBlockN * krow_bytes;
     const int lim = kv_len - 1 - t * kBlockN;
 #pragma unroll
@@ -226,7 +248,7 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
     }
   };
   auto dma_v = [&](int t, const char* st) {
-    t = min(t, ntiles - 1);
+    t = tile_of(t);
     const char* vt = vbytes + (int64_t)t * C::kVTile;
 #pragma unroll
     for (int i = 0; i < C::kVDma; ++i) dma16(vt + vdma_off[i], lds_addr(st) + (wave_u * C::kVDma + i) * 1024);
@@ -279,10 +301,12 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
         }
     }
   };
-  // scores of keys past kv_len to -inf (only the last tile can hold such keys)
+  // scores of keys past kv_len to -inf (only the last key tile can hold such keys)
   const bool ragged = (kv_len & (kBlockN - 1)) != 0;
   auto mask_tail = [&](int t, f32x16 (&s)[QB][2]) {
-    if (t == ntiles - 1 && ragged) {
+    const bool last = SPARSE ? t < ntiles && tile_of(t) == ktiles - 1 : t == ntiles - 1;
+    if (last && ragged) {
+      if constexpr (SPARSE) t = tile_of(t);
       // keeps the compiler from executing this block unconditionally with selects
       asm volatile("");
 #pragma unroll
@@ -593,13 +617,14 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   }
 }
 
-template <int D, int QB, int WAVES, int NST, bool ROPE, bool QK8>
+template <int D, int QB, int WAVES, int NST, bool ROPE, bool QK8, bool SPARSE = false>
 hipError_t launch_fwd_t(AttnArgs a, hipStream_t s) {
   using C = FwdCfg<D, QB, WAVES, QK8>;
   a.n_qtiles = (a.nq + C::kBlockM - 1) / C::kBlockM;
   const int64_t nwg = (int64_t)a.n_qtiles * a.hc * a.batch;
   if (nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, QB, WAVES, NST, ROPE, QK8>), dim3((unsigned)nwg), dim3(C::kThreads), 0, s, a);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, QB, WAVES, NST, ROPE, QK8, SPARSE>), dim3((unsigned)nwg), dim3(C::kThreads),
+                     0, s, a);
   return hipGetLastError();
 }
 
@@ -625,6 +650,18 @@ hipError_t launch_attn_fwd(const AttnArgs& a, int head_dim, bool rope_q, bool qk
       return rope_q ? launch_fwd_t<64, 1, 4, 2, true, false>(a, s) : launch_fwd_t<64, 1, 4, 2, false, false>(a, s);
     return rope_q ? launch_fwd_t<64, 1, 8, 4, true, false>(a, s) : launch_fwd_t<64, 1, 8, 4, false, false>(a, s);
   }
+  return hipErrorInvalidValue;
+}
+
+// Block-sparse attention: two waves (64 queries, one query tile) per workgroup
+// and two K/V stages, so two workgroups share a CU.
+hipError_t launch_attn_sparse(const AttnArgs& a, int head_dim, hipStream_t s) {
+  if (a.batch <= 0 || a.batch > kMaxBatch || a.hc <= 0 || !a.tiles || a.keep < 1 || a.keep > kVsaMaxKeep)
+    return hipErrorInvalidValue;
+  for (int b = 0; b < a.batch; ++b)
+    if (a.kv_len[b] < 1 || a.keep > (a.kv_len[b] + kBlockN - 1) / kBlockN) return hipErrorInvalidValue;
+  if (head_dim == 128) return launch_fwd_t<128, 1, 2, 2, false, false, true>(a, s);
+  if (head_dim == 64) return launch_fwd_t<64, 1, 2, 2, false, false, true>(a, s);
   return hipErrorInvalidValue;
 }
 

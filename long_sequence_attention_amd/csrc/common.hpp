@@ -103,6 +103,11 @@ constexpr int kQK8MaxTiles = 4096;
 // workgroup on the CU hides them.
 constexpr int kSmallKeys = 1024;
 
+// Block-sparse attention over 64-token tiles (one query tile = one workgroup of
+// the sparse attention kernel, one key tile = one K/V tile).
+constexpr int kVsaMaxTiles = 8192;  // key tiles one selection can rank (64 KB of LDS sort keys)
+constexpr int kVsaMaxKeep = 4096;   // kept tiles per query tile (the attention kernel's LDS list)
+
 // Element offsets of batch entry b are b * (the *_batch stride) on top of those below.
 struct AttnArgs {
   const __bf16* q;       // q of head `head_begin`, token 0, entry 0
@@ -134,6 +139,10 @@ struct AttnArgs {
   const float* ksc;      // k scales, [bh][nk_pad / 64]
   int32_t nq_blocks;
   int32_t nk_blocks;
+  // block-sparse attention: key tiles kept by each (entry, head, query tile),
+  // [bh][n_qtiles][keep], ascending
+  const int32_t* tiles;
+  int32_t keep;
   int32_t kv_len[kMaxBatch];  // valid keys of each entry
 };
 
@@ -174,8 +183,32 @@ struct PrepArgs {
   int32_t kv_len[kMaxBatch];
 };
 
+// Tile means of q or k for the block-sparse selection: float32 [bh][tiles][d].
+struct VsaMeanArgs {
+  const __bf16* x;  // head `head_begin`, token 0, entry 0
+  int64_t row;      // elements between consecutive tokens
+  int64_t batch;    // elements between batch entries
+  float* mean;
+  int32_t n;        // tokens
+  int32_t tiles;    // ceil(n / 64)
+  int32_t hc;
+  int32_t bh;       // entries * hc
+};
+
+// Coarse scores [bh][tq][tk] of the tile means, and the kept tiles [bh][tq][keep].
+struct VsaSelectArgs {
+  const float* qm;  // [bh][tq][d]
+  const float* km;  // [bh][tk][d]
+  float* s;         // [bh][tq][tk]
+  int32_t* tiles;   // [bh][tq][keep]
+  int32_t tq, tk, keep, d, bh;
+};
+
 // Host-side launchers (defined in the kernel translation units).
 hipError_t launch_attn_fwd(const AttnArgs& a, int head_dim, bool rope_q, bool qk_int8, hipStream_t s);
+hipError_t launch_attn_sparse(const AttnArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_vsa_means(const VsaMeanArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_vsa_select(const VsaSelectArgs& a, hipStream_t s);
 hipError_t launch_prepare(const PrepArgs& a, int head_dim, bool rope_k, hipStream_t s);
 hipError_t launch_quantize(const QuantArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_pack(const void* src, void* dst, int64_t n, int32_t ht, int32_t d, int32_t groups,

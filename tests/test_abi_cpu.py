@@ -34,7 +34,7 @@ def header_functions():
 
 def test_library_exports_every_declared_symbol(lib):
     names = header_functions()
-    assert len(names) == 14
+    assert len(names) == 19
     assert sorted(names) == sorted(_lib.SIGNATURES)
     for n in names:
         assert hasattr(lib, n), n
@@ -143,6 +143,12 @@ def test_handle_checks_without_device(lib):
     assert lib.vdit_attn_prepare_lens(bogus, None, None, None, lens, None, 0, None) == INVALID
     assert lib.vdit_attn_attend_lens(bogus, None, None, None, lens, None, None, 0, None) == INVALID
     assert lib.vdit_attn_rope_probe(bogus, None, None) == INVALID
+    k = ctypes.c_int32()
+    assert lib.vdit_vsa_keep(bogus, 0.8, ctypes.byref(k)) == INVALID
+    assert lib.vdit_vsa_workspace_bytes(bogus, 3, ctypes.byref(n)) == INVALID
+    assert lib.vdit_vsa_select(bogus, None, None, 3, None, None, 0, None) == INVALID
+    assert lib.vdit_vsa_attend(bogus, None, None, None, 3, None, None, None, 0, None) == INVALID
+    assert lib.vdit_vsa_fwd(bogus, None, None, None, 3, None, None, 0, None) == INVALID
 
 
 def test_pack_validation_without_device(lib):
