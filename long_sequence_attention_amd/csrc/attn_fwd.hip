@@ -21,9 +21,12 @@
 // SIMD are kept half an iteration apart (one forms scores and weights while the
 // other runs products), so the SIMD's matrix and vector units overlap.
 //
-// Block-sparse mode (SPARSE): the workgroup is one 64-query tile (two waves) and
-// visits only the key tiles listed for it, in list order; everything else is the
-// same per wave.
+// Block-sparse mode (SPARSE): the workgroup is one 64-query tile and visits only
+// the key tiles listed for it, in list order. Four waves split it: wave w takes
+// queries 32 (w / 2) .. + 31 and keys 32 (w % 2) .. + 31 of every tile, with its
+// own softmax reference, row sums and accumulators; the two waves of a query
+// block merge their partial results at the end. So two waves share each SIMD,
+// as in the dense kernel, although one query tile is only 64 rows.
 //
 // Softmax: the weights use a fixed reference, the row maximum of the first key
 // tile, in the log2 domain (c = scale * log2 e): p = 2^(s*c - m). O is never
@@ -71,11 +74,12 @@ __device__ __forceinline__ uint32_t lds_addr(const char* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
 }
 
-template <int D, int QB, int WAVES, bool QK8 = false>
+template <int D, int QB, int WAVES, bool QK8 = false, int KS = 1>
 struct FwdCfg {
   static constexpr int kWaves = WAVES;
   static constexpr int kThreads = kWaves * kWave;
-  static constexpr int kBlockM = kWaves * QB * 32;
+  static constexpr int kKSplit = KS;                     // waves sharing the keys of each query row
+  static constexpr int kBlockM = kWaves / KS * QB * 32;
   static constexpr int kKRow = QK8 ? D : D * 2;          // bytes per K row in LDS (int8 or bf16)
   static constexpr int kKChunks = kKRow / 16;            // 16-byte chunks per K row
   static constexpr int kVRow = kBlockN * 2;              // bytes per V^T row in LDS
@@ -100,7 +104,9 @@ struct FwdCfg {
 // one conversion per score more than with bfloat16 q.k.
 template <int D, int QB, int WAVES, int NST, bool ROPE, bool QK8, bool SPARSE>
 __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
-  using C = FwdCfg<D, QB, WAVES, QK8>;
+  constexpr int KS = SPARSE ? 2 : 1;  // waves per query block (key split)
+  constexpr int KH = 2 / KS;          // 32-key blocks per wave and tile
+  using C = FwdCfg<D, QB, WAVES, QK8, KS>;
   using QFrag = typename std::conditional<QK8, i32x4, bf16x8>::type;
   static_assert(!(QK8 && ROPE), "int8 q.k takes no RoPE");
   static_assert(!SPARSE || (!QK8 && !ROPE && C::kBlockM == 64), "block-sparse: bfloat16, 64-query tiles");
@@ -144,11 +150,13 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hl = lane >> 5;
+  const int qw = wave / KS;               // query block of the wave
+  const int kblk0 = KS == 2 ? wave & 1 : 0;  // first 32-key block of each tile it takes
 
   if (tid == 0) wg_retry = 0;
 
   // ---- this wave's queries into registers (B operand layout), RoPE fused
-  const int q0 = qtile * C::kBlockM + wave * QB * 32;
+  const int q0 = qtile * C::kBlockM + qw * QB * 32;
   QFrag qf[QB][C::kDK];
   float cq[QB];  // factor of the float scores in the exponent (log2 domain)
 #pragma unroll
@@ -255,15 +263,16 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   };
 
   // per-lane LDS read offsets: the XOR swizzle depends only on the lane and the
-  // k-step, so the stage base and the 32-row block fold into the immediate offset
-  int koff[C::kDK], voff[4];
+  // k-step, so the stage base and the 32-row block fold into the immediate offset.
+  // voff[g]: the wave's g-th group of 16 keys (groups 2 kblk0 .. of the tile).
+  int koff[C::kDK], voff[2 * KH];
   {
     const int kswz = l32 & (C::kKChunks - 1);
     const int vswz = (l32 >> 1) & 7;
 #pragma unroll
     for (int kk = 0; kk < C::kDK; ++kk) koff[kk] = l32 * C::kKRow + (((2 * kk + hl) ^ kswz) << 4);
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) voff[s4] = l32 * C::kVRow + (((2 * s4 + hl) ^ vswz) << 4);
+    for (int s4 = 0; s4 < 2 * KH; ++s4) voff[s4] = l32 * C::kVRow + (((2 * (s4 + 2 * kblk0) + hl) ^ vswz) << 4);
   }
 
   // S^T = K * Q^T for the K tile in `kl`
@@ -276,14 +285,16 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
     else
       return __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qv, acc, 0, 0, 0);
   };
-  auto scores = [&](const char* kl, f32x16 (&s)[QB][2]) {
+  auto scores = [&](const char* kl, f32x16 (&s)[QB][KH]) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) { s[qb][0] = f32x16{}; s[qb][1] = f32x16{}; }
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < KH; ++kb) s[qb][kb] = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < C::kDK; ++kk) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const QFrag ka = *reinterpret_cast<const QFrag*>(kl + kb * 32 * C::kKRow + koff[kk]);
+      for (int kb = 0; kb < KH; ++kb) {
+        const QFrag ka = *reinterpret_cast<const QFrag*>(kl + (kb + kblk0) * 32 * C::kKRow + koff[kk]);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) s[qb][kb] = qk_mfma(ka, qf[qb][kk], s[qb][kb]);
       }
@@ -292,7 +303,7 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < KH; ++kb) {
           const i32x16 iv = __builtin_bit_cast(i32x16, s[qb][kb]);
           f32x16 fv;
 #pragma unroll
@@ -303,7 +314,7 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   };
   // scores of keys past kv_len to -inf (only the last key tile can hold such keys)
   const bool ragged = (kv_len & (kBlockN - 1)) != 0;
-  auto mask_tail = [&](int t, f32x16 (&s)[QB][2]) {
+  auto mask_tail = [&](int t, f32x16 (&s)[QB][KH]) {
     const bool last = SPARSE ? t < ntiles && tile_of(t) == ktiles - 1 : t == ntiles - 1;
     if (last && ragged) {
       if constexpr (SPARSE) t = tile_of(t);
@@ -312,23 +323,25 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < KH; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = t * kBlockN + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+            const int key = t * kBlockN + (kb + kblk0) * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
             if (key >= kv_len) s[qb][kb][r] = -__builtin_inff();
           }
     }
   };
   // maximum of the scores of each query in the tile (both lane halves), times c
-  auto tile_max = [&](const f32x16 (&s)[QB][2], const float (&ct)[QB], float (&m)[QB]) {
+  auto tile_max = [&](const f32x16 (&s)[QB][KH], const float (&ct)[QB], float (&m)[QB]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float mx = s[qb][0][0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[qb][0][r]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][1][r]);
+      for (int kb = 1; kb < KH; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       m[qb] = mx * ct[qb];
     }
@@ -351,36 +364,35 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   // empty asm statements pin values to their group where the compiler would
   // otherwise sink their computation into a later block. Per accumulator the
   // products run in the order of scores() above.
-  constexpr int kNS = 2 * C::kDK;
-  constexpr int kNP = 4 * C::kDB;
+  constexpr int kNS = KH * C::kDK;
+  constexpr int kNP = 2 * KH * C::kDB;
   constexpr int kR = 4;
-  constexpr int kPairs = 16;                 // float16 pairs of weights per lane
+  constexpr int kPairs = 8 * KH;             // float16 pairs of weights per lane
   constexpr int kPPG = kPairs / kNS;         // pairs per score product
   static_assert(kNS >= kR && kNP >= kR && kPairs % kNS == 0 && kPairs % kNP == 0, "pipeline shape");
   auto kfrag = [&](const char* kl, int j) {
-    return *reinterpret_cast<const QFrag*>(kl + (j & 1) * 32 * C::kKRow + koff[j >> 1]);
+    return *reinterpret_cast<const QFrag*>(kl + (j % KH + kblk0) * 32 * C::kKRow + koff[j / KH]);
   };
   auto vfrag = [&](const char* vl, int j) {
     return *reinterpret_cast<const f16x8*>(vl + (j % C::kDB) * 32 * C::kVRow + voff[j / C::kDB]);
   };
   // scores of the next tile with the weights of the held one; leaves the first
   // kR V^T fragments of the products in `vr`
-  auto score_phase = [&](const char* k_read, const char* v_read, const f32x16 (&s_cur)[QB][2],
-                         f32x16 (&s_next)[QB][2], const float (&ccur)[QB], const float (&mref)[QB],
-                         f16x8 (&vr)[kR], f16x8 (&pf)[QB][4], f16x2 (&hv)[QB][kPairs]) {
+  auto score_phase = [&](const char* k_read, const char* v_read, const f32x16 (&s_cur)[QB][KH],
+                         f32x16 (&s_next)[QB][KH], const float (&ccur)[QB], const float (&mref)[QB],
+                         f16x8 (&vr)[kR], f16x8 (&pf)[QB][2 * KH], f16x2 (&hv)[QB][kPairs]) {
     QFrag kr[kR];
-    u32x4 bits[QB][4];
+    u32x4 bits[QB][2 * KH];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      s_next[qb][0] = f32x16{};
-      s_next[qb][1] = f32x16{};
-    }
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < KH; ++kb) s_next[qb][kb] = f32x16{};
 #pragma unroll
     for (int j = 0; j < kR; ++j) kr[j] = kfrag(k_read, j);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int g = 0; g < kNS; ++g) {
-      const int kk = g >> 1, kb = g & 1;
+      const int kk = g / KH, kb = g % KH;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
         s_next[qb][kb] = qk_mfma(kr[g % kR], qf[qb][kk], s_next[qb][kb]);
@@ -409,19 +421,19 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) pf[qb][s4] = __builtin_bit_cast(f16x8, bits[qb][s4]);
+      for (int s4 = 0; s4 < 2 * KH; ++s4) pf[qb][s4] = __builtin_bit_cast(f16x8, bits[qb][s4]);
   };
   // O^T += V^T P^T; the row sums of the rounded weights (v_dot2) ride along with
   // the products, which have no other vector work
   // with int8 q.k this also converts the integer scores of the next tile to
   // float, two per product
-  auto product_phase = [&](const char* v_read, f16x8 (&vr)[kR], const f16x8 (&pf)[QB][4],
-                           const f16x2 (&hv)[QB][kPairs], f32x16 (&s_next)[QB][2]) {
-    float lsum[QB][4];
+  auto product_phase = [&](const char* v_read, f16x8 (&vr)[kR], const f16x8 (&pf)[QB][2 * KH],
+                           const f16x2 (&hv)[QB][kPairs], f32x16 (&s_next)[QB][KH]) {
+    float lsum[QB][2 * KH];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) lsum[qb][s4] = 0.0f;
+      for (int s4 = 0; s4 < 2 * KH; ++s4) lsum[qb][s4] = 0.0f;
 #pragma unroll
     for (int g = 0; g < kNP; ++g) {
       const int s4 = g / C::kDB, db = g % C::kDB;
@@ -451,7 +463,12 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) l_run[qb] += (lsum[qb][0] + lsum[qb][1]) + (lsum[qb][2] + lsum[qb][3]);
+    for (int qb = 0; qb < QB; ++qb) {
+      if constexpr (KH == 2)
+        l_run[qb] += (lsum[qb][0] + lsum[qb][1]) + (lsum[qb][2] + lsum[qb][3]);
+      else
+        l_run[qb] += lsum[qb][0] + lsum[qb][1];
+    }
   };
 
   // direct loads issued per iteration by one wave
@@ -459,7 +476,7 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
 
   // Stage the first tiles (K 0..3 and V 0..1, or K 0..1 and V 0 with two
   // stages) and form the scores of tile 0.
-  f32x16 s_a[QB][2], s_b[QB][2];
+  f32x16 s_a[QB][KH], s_b[QB][KH];
   float c_a[QB], c_b[QB];
   auto prologue = [&]() {
     if constexpr (QK8) {
@@ -514,13 +531,13 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
     barrier_only();
   };
   // c_cur / c_next: exponent factors of the scores held for tiles t and t+1
-  auto step = [&](int t, char* k_read, char* k_fill, char* v_read, char* v_fill, f32x16 (&s_cur)[QB][2],
-                  f32x16 (&s_next)[QB][2], const float (&c_cur)[QB], float (&c_next)[QB],
+  auto step = [&](int t, char* k_read, char* k_fill, char* v_read, char* v_fill, f32x16 (&s_cur)[QB][KH],
+                  f32x16 (&s_next)[QB][KH], const float (&c_cur)[QB], float (&c_next)[QB],
                   const float (&mref)[QB]) {
     dma_v(t + NST / 2, v_fill);
     dma_k(t + NST, k_fill);
     f16x8 vr[kR];
-    f16x8 pf[QB][4];
+    f16x8 pf[QB][2 * KH];
     f16x2 hv[QB][kPairs];
     score_phase(k_read, v_read, s_cur, s_next, c_cur, mref, vr, pf, hv);
     if (upper) sync();
@@ -559,6 +576,10 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   float mref[QB];
   tile_max(s_a, c_a, mref);
   main_pass(mref);
+  // reference of the weights in o and l_run (the retry below replaces it)
+  float mfin[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) mfin[qb] = mref[qb];
 
   // ---- rare path: some weight left the float16 range (a later key scored far
   // above the first tile's maximum) or the inputs were not finite. The whole
@@ -582,7 +603,7 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
       dma_k(t, k_st0);
       wait_vm<0>();
       barrier_only();
-      f32x16 s[QB][2];
+      f32x16 s[QB][KH];
       scores(k_st0, s);
       mask_tail(t, s);
       float ct[QB], m[QB];
@@ -594,12 +615,58 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
     }
     prologue();
     main_pass(mx);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) mfin[qb] = mx[qb];
+  }
+
+  // ---- key split: the wave with the second key half hands its row sums,
+  // references and accumulators to the first through LDS (the stages are free
+  // now); the first merges them, p = 2^(s*c - m) from both sides rescaled to the
+  // larger reference. A side whose keys were all masked (reference -inf: only a
+  // ragged last tile can give it) adds nothing.
+  if constexpr (KS == 2) {
+    float* xo = reinterpret_cast<float*>(qw == 0 ? k_st0 : v_st0);  // [QB][kDB][16][64 lanes]
+    float* xl = reinterpret_cast<float*>(qw == 0 ? k_st1 : v_st1);  // [QB][2][64 lanes]
+    if (kblk0 == 1) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        xl[(qb * 2) * 64 + lane] = l_run[qb] + __shfl_xor(l_run[qb], 32);
+        xl[(qb * 2 + 1) * 64 + lane] = mfin[qb];
+#pragma unroll
+        for (int db = 0; db < C::kDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) xo[((qb * C::kDB + db) * 16 + r) * 64 + lane] = o[qb][db][r];
+      }
+    }
+    __syncthreads();
+    if (kblk0 == 1) return;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float l0 = l_run[qb] + __shfl_xor(l_run[qb], 32);
+      const float l1 = xl[(qb * 2) * 64 + lane];
+      const float m0 = mfin[qb];
+      const float m1 = xl[(qb * 2 + 1) * 64 + lane];
+      const bool v0 = m0 > -__builtin_inff(), v1 = m1 > -__builtin_inff();
+      const float mm = fmaxf(v0 ? m0 : -__builtin_inff(), v1 ? m1 : -__builtin_inff());
+      const float a0 = v0 ? __builtin_amdgcn_exp2f(m0 - mm) : 0.0f;
+      const float a1 = v1 ? __builtin_amdgcn_exp2f(m1 - mm) : 0.0f;
+      const float lt = (v0 ? a0 * l0 : 0.0f) + (v1 ? a1 * l1 : 0.0f);
+      // the merged weights are those of the reference mm: the epilogue divides by lt
+      l_run[qb] = lt;
+#pragma unroll
+      for (int db = 0; db < C::kDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float x1 = xo[((qb * C::kDB + db) * 16 + r) * 64 + lane];
+          o[qb][db][r] = (v0 ? a0 * o[qb][db][r] : 0.0f) + (v1 ? a1 * x1 : 0.0f);
+        }
+    }
   }
 
   // ---- epilogue: normalise, round to bf16, store [nq, hc, d]
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float lt = l_run[qb] + __shfl_xor(l_run[qb], 32);
+    const float lt = KS == 2 ? l_run[qb] : l_run[qb] + __shfl_xor(l_run[qb], 32);
     const float inv = 1.0f / lt;
     const int qi = q0 + qb * 32 + l32;
     if (qi < a.nq) {
@@ -619,7 +686,7 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
 
 template <int D, int QB, int WAVES, int NST, bool ROPE, bool QK8, bool SPARSE = false>
 hipError_t launch_fwd_t(AttnArgs a, hipStream_t s) {
-  using C = FwdCfg<D, QB, WAVES, QK8>;
+  using C = FwdCfg<D, QB, WAVES, QK8, SPARSE ? 2 : 1>;
   a.n_qtiles = (a.nq + C::kBlockM - 1) / C::kBlockM;
   const int64_t nwg = (int64_t)a.n_qtiles * a.hc * a.batch;
   if (nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidValue;
@@ -653,15 +720,15 @@ hipError_t launch_attn_fwd(const AttnArgs& a, int head_dim, bool rope_q, bool qk
   return hipErrorInvalidValue;
 }
 
-// Block-sparse attention: two waves (64 queries, one query tile) per workgroup
-// and two K/V stages, so two workgroups share a CU.
+// Block-sparse attention: four waves (64 queries = one query tile, keys split in
+// halves) per workgroup and two K/V stages, so two workgroups share a CU.
 hipError_t launch_attn_sparse(const AttnArgs& a, int head_dim, hipStream_t s) {
   if (a.batch <= 0 || a.batch > kMaxBatch || a.hc <= 0 || !a.tiles || a.keep < 1 || a.keep > kVsaMaxKeep)
     return hipErrorInvalidValue;
   for (int b = 0; b < a.batch; ++b)
     if (a.kv_len[b] < 1 || a.keep > (a.kv_len[b] + kBlockN - 1) / kBlockN) return hipErrorInvalidValue;
-  if (head_dim == 128) return launch_fwd_t<128, 1, 2, 2, false, false, true>(a, s);
-  if (head_dim == 64) return launch_fwd_t<64, 1, 2, 2, false, false, true>(a, s);
+  if (head_dim == 128) return launch_fwd_t<128, 1, 4, 2, false, false, true>(a, s);
+  if (head_dim == 64) return launch_fwd_t<64, 1, 4, 2, false, false, true>(a, s);
   return hipErrorInvalidValue;
 }
 
