@@ -84,51 +84,51 @@ def run_nhd(dev, q, k, v, *, head_begin=0, head_count=None, key_len=None, scale=
 # The five workloads
 # ---------------------------------------------------------------------------
 
-def test_cfg1_small_d64_all_rows(dev):
-    note("cfg1 N=256 H=2 d=64 seed 1001")
+def test_n256_h2_d64_all_rows(dev):
+    note("self-attention N=256 H=2 d=64 seed 1001")
     q, k, v = nhd_inputs(256, 256, 2, 64, 1001)
     out = run_nhd(dev, q, k, v)
-    check(as_f64(out), oracle.mha_reference(q, k, v), "cfg1")
+    check(as_f64(out), oracle.mha_reference(q, k, v), "N=256 H=2 d=64")
 
 
-def test_cfg2_n4096_h10_all_rows(dev):
-    note("cfg2 N=4096 H=10 d=128 seed 1002")
+def test_n4096_h10_all_rows(dev):
+    note("self-attention N=4096 H=10 d=128 seed 1002")
     q, k, v = nhd_inputs(4096, 4096, 10, 128, 1002)
     out = run_nhd(dev, q, k, v)
-    check(as_f64(out), oracle.mha_reference(q, k, v), "cfg2")
+    check(as_f64(out), oracle.mha_reference(q, k, v), "N=4096 H=10")
 
 
 @pytest.mark.timeout(900)
-def test_cfg3_ulysses_share_n75600(dev):
+def test_ulysses_share_n75600(dev):
     n = 21 * 45 * 80
-    note(f"cfg3 N={n} Ht=40 heads 0-9 d=128 seed 1003")
+    note(f"Ulysses share N={n} Ht=40 heads 0-9 d=128 seed 1003")
     q, k, v = nhd_inputs(n, n, 40, 128, 1003)
     out = run_nhd(dev, q, k, v, head_begin=0, head_count=10)
     rows = si.sample_rows(n, 4096, 1003, si.tile_edge_rows(n))
     got = as_f64(out[torch.from_numpy(rows).to(dev)])
     ref = oracle.mha_reference(q, k, v, head_begin=0, head_count=10, rows=rows)
-    check(got, ref, f"cfg3 ({len(rows)} rows x 10 heads)")
+    check(got, ref, f"N={n} heads 0-9 ({len(rows)} rows x 10 heads)")
 
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("fixed_len", [None, 64, 512])
-def test_cfg4_cross_attention_key_mask(dev, fixed_len):
+def test_text_cross_attention_key_mask(dev, fixed_len):
     nq, nk = 75600, 512
     L = si.key_length(1004) if fixed_len is None else fixed_len
-    note(f"cfg4 Nq={nq} Nk={nk} L={L} H=40 d=128 seed 1004")
+    note(f"text cross-attention Nq={nq} Nk={nk} L={L} H=40 d=128 seed 1004")
     q, k, v = nhd_inputs(nq, nk, 40, 128, 1004)
     out = run_nhd(dev, q, k, v, key_len=L)
     rows = si.sample_rows(nq, 4096, 1004, si.tile_edge_rows(nq))
     got = as_f64(out[torch.from_numpy(rows).to(dev)])
     ref = oracle.mha_reference(q, k, v, rows=rows, key_len=L)
-    check(got, ref, f"cfg4 L={L}")
+    check(got, ref, f"text cross-attention L={L}")
 
 
 @pytest.mark.timeout(1200)
-def test_cfg5_packed_rope_n131072(dev):
+def test_packed_rope_n131072(dev):
     vd = vdm()
     n = 32 * 64 * 64
-    note(f"cfg5 packed N={n} H=40 d=128 RoPE 44/42/42 sigma=0.5 seed 1005")
+    note(f"packed RoPE N={n} H=40 d=128 bands 44/42/42 sigma=0.5 seed 1005")
     qkv = si.normal_bf16((n, 3, 40, 128), 1005, si.STREAM_Q, 0.5)
     attn = vd.Attention(n, n, 40, 128, layout="N3HD", rope=ROPE5)
     out = attn.forward(up(qkv, dev))
@@ -137,7 +137,7 @@ def test_cfg5_packed_rope_n131072(dev):
     got = as_f64(out[torch.from_numpy(rows).to(dev)])
     del out
     ref = oracle.mha_reference(qkv, layout="N3HD", rows=rows, rope=ROPE5)
-    check(got, ref, f"cfg5 ({len(rows)} rows x 40 heads)")
+    check(got, ref, f"packed RoPE N={n} ({len(rows)} rows x 40 heads)")
 
 
 # ---------------------------------------------------------------------------
