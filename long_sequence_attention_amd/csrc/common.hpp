@@ -105,7 +105,7 @@ constexpr int kSmallKeys = 1024;
 
 // Block-sparse attention over 64-token tiles (one query tile = one workgroup of
 // the sparse attention kernel, one key tile = one K/V tile).
-constexpr int kVsaMaxTiles = 8192;  // key tiles one selection can rank (64 KB of LDS sort keys)
+constexpr int kVsaMaxTiles = 8192;  // key tiles one selection can rank (32 keys per thread of the select kernel)
 constexpr int kVsaMaxKeep = 4096;   // kept tiles per query tile (the attention kernel's LDS list)
 
 // Element offsets of batch entry b are b * (the *_batch stride) on top of those below.

@@ -7,7 +7,7 @@
 // scores are float32 products and sums in dimension order (no fused
 // multiply-add), -0 counts as +0 and NaN as the lowest score, and equal scores
 // keep the lower tile index. These kernels are small next to the attention (a
-// few percent of its time at sparsity 0.8) and are written for clarity.
+// few percent of its time at sparsity 0.8).
 #include "common.hpp"
 
 namespace vdit {
@@ -82,54 +82,118 @@ __global__ void __launch_bounds__(256) vsa_score_kernel(VsaSelectArgs a) {
     }
 }
 
-// Ascending bitonic sort of n (a power of two) 64-bit keys in LDS by the whole
-// workgroup; every thread handles n / 2 / blockDim.x compare-exchanges per pass.
-__device__ void bitonic_sort(uint64_t* keys, int n) {
-  for (int k = 2; k <= n; k <<= 1)
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int t = threadIdx.x; t < n / 2; t += blockDim.x) {
-        const int i = ((t & ~(j - 1)) << 1) | (t & (j - 1));  // bit j of i is clear
-        const int l = i + j;
-        const uint64_t x = keys[i], y = keys[l];
-        if ((x > y) == ((i & k) == 0)) {
-          keys[i] = y;
-          keys[l] = x;
-        }
-      }
-      __syncthreads();
-    }
+// Block-wide inclusive prefix sum of one value per thread (256 threads).
+__device__ uint32_t block_scan(uint32_t v, uint32_t* wtot) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t n = __shfl_up(v, o);
+    if (lane >= o) v += n;
+  }
+  if (lane == 63) wtot[w] = v;
+  __syncthreads();
+  uint32_t add = 0;
+#pragma unroll
+  for (int k = 0; k < 3; ++k) add += k < w ? wtot[k] : 0u;
+  __syncthreads();
+  return v + add;
 }
 
-// One workgroup per (query tile, entry * head). Key of tile j: the score mapped
-// to an unsigned integer of the same order, complemented (highest score first),
-// in the upper 32 bits and j in the lower, so an ascending sort ranks by score
-// and then by tile index. The first `keep` keys are the kept tiles; a second
-// sort puts their indices in ascending order.
-__global__ void __launch_bounds__(256) vsa_select_kernel(VsaSelectArgs a, int p2) {
-  extern __shared__ uint64_t keys[];
+// Exclusive rank of a true flag among the true flags of lower threads, and the
+// block's total (256 threads).
+__device__ uint32_t flag_rank(bool f, uint32_t* wtot, uint32_t& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint64_t m = __ballot(f);
+  const uint32_t below = (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
+  if (lane == 0) wtot[w] = (uint32_t)__popcll(m);
+  __syncthreads();
+  uint32_t off = 0, tot = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t x = wtot[k];
+    off += k < w ? x : 0u;
+    tot += x;
+  }
+  __syncthreads();
+  total = tot;
+  return off + below;
+}
+
+constexpr int kSelThreads = 256;
+constexpr int kSelPerThread = kVsaMaxTiles / kSelThreads;
+
+// One workgroup per (query tile, entry * head). Thread t holds the keys of
+// tiles t, t + 256, ...: the score mapped to an unsigned integer whose order is
+// the reverse of the score order, so the kept tiles are the `keep` smallest keys
+// (equal keys: lower tile first). A radix select over the four 8-bit digits,
+// most significant first (a histogram of the keys that match the digits found
+// so far, then the bin holding the wanted rank), gives the value of the
+// keep-th smallest key and how many keys equal to it are kept; a pass in tile
+// order then writes the kept tiles ascending.
+__global__ void __launch_bounds__(kSelThreads) vsa_select_kernel(VsaSelectArgs a) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t wtot[4];
+  __shared__ uint32_t found[2];
+  const int tid = threadIdx.x;
   const int i = blockIdx.x;
   const int bh = blockIdx.y;
   const float* row = a.s + ((int64_t)bh * a.tq + i) * a.tk;
-  for (int j = threadIdx.x; j < p2; j += blockDim.x) {
-    uint64_t key = ~0ull;
+  const int per = (a.tk + kSelThreads - 1) / kSelThreads;
+  uint32_t key[kSelPerThread];
+#pragma unroll
+  for (int c = 0; c < kSelPerThread; ++c) {
+    const int j = c * kSelThreads + tid;
+    uint32_t kv = 0xffffffffu;  // above every score's key
     if (j < a.tk) {
       float v = __fadd_rn(row[j], 0.0f);  // -0 -> +0
       if (v != v) v = -__builtin_inff();
       uint32_t u = __float_as_uint(v);
-      u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-      key = ((uint64_t)(~u) << 32) | (uint32_t)j;
+      u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // ascending with the score
+      kv = ~u;
     }
-    keys[j] = key;
+    key[c] = kv;
   }
-  __syncthreads();
-  bitonic_sort(keys, p2);
-  int pk = 1;
-  while (pk < a.keep) pk <<= 1;
-  for (int p = threadIdx.x; p < pk; p += blockDim.x) keys[p] = p < a.keep ? (keys[p] & 0xffffffffull) : ~0ull;
-  __syncthreads();
-  bitonic_sort(keys, pk);
+  uint32_t prefix = 0, r = (uint32_t)a.keep;  // r: rank still wanted among keys matching prefix
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int sh = 24 - 8 * p;
+    hist[tid] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < kSelPerThread; ++c) {
+      const uint32_t k = key[c];
+      const bool match = c * kSelThreads + tid < a.tk && (p == 0 || ((k ^ prefix) >> (sh + 8)) == 0);
+      if (match) atomicAdd(&hist[(k >> sh) & 255u], 1u);
+    }
+    __syncthreads();
+    const uint32_t cnt = hist[tid];
+    const uint32_t incl = block_scan(cnt, wtot);
+    if (incl - cnt < r && r <= incl) {
+      found[0] = (uint32_t)tid;
+      found[1] = r - (incl - cnt);
+    }
+    __syncthreads();
+    prefix |= found[0] << sh;
+    r = found[1];
+    __syncthreads();
+  }
   int32_t* o = a.tiles + ((int64_t)bh * a.tq + i) * a.keep;
-  for (int p = threadIdx.x; p < a.keep; p += blockDim.x) o[p] = (int32_t)keys[p];
+  uint32_t base_eq = 0, base_out = 0;
+#pragma unroll
+  for (int c = 0; c < kSelPerThread; ++c) {
+    if (c < per) {  // the same for every thread: the barriers inside stay uniform
+      const int j = c * kSelThreads + tid;
+      const bool valid = j < a.tk;
+      const bool eq = valid && key[c] == prefix;
+      uint32_t n_eq, n_kept;
+      const uint32_t rank_eq = base_eq + flag_rank(eq, wtot, n_eq);
+      const bool kept = valid && (key[c] < prefix || (eq && rank_eq < r));
+      const uint32_t pos = base_out + flag_rank(kept, wtot, n_kept);
+      if (kept) o[pos] = j;
+      base_eq += n_eq;
+      base_out += n_kept;
+    }
+  }
 }
 
 }  // namespace
@@ -154,9 +218,7 @@ hipError_t launch_vsa_select(const VsaSelectArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(vsa_score_kernel, sgrid, dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  int p2 = 2;
-  while (p2 < a.tk) p2 <<= 1;
-  hipLaunchKernelGGL(vsa_select_kernel, dim3((unsigned)a.tq, (unsigned)a.bh), dim3(256), (size_t)p2 * 8, s, a, p2);
+  hipLaunchKernelGGL(vsa_select_kernel, dim3((unsigned)a.tq, (unsigned)a.bh), dim3(kSelThreads), 0, s, a);
   return hipGetLastError();
 }
 

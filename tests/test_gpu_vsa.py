@@ -94,6 +94,45 @@ def test_selection_and_output_match_oracle(dev, n, ht, d, h0, hc, keep, seed):
     check(as_f64(out), ref, f"vsa n={n} keep={keep}")
 
 
+def test_selection_with_many_ties_across_chunks(dev):
+    """600 key tiles (the select kernel holds them in chunks of 256 per thread block)
+    whose tiles are constant vectors of small integers, so the coarse scores are
+    small exact integers with many ties: the kept tiles must still equal the
+    oracle's, ties going to the lower tile."""
+    vd = vdm()
+    n, d, keep = 64 * 600, 64, 100
+    rng = np.random.default_rng(3050)
+    qt = rng.integers(-1, 2, (600, 1, 4)).astype(np.float32)
+    kt = rng.integers(0, 3, (600, 1, 4)).astype(np.float32)
+    q = np.zeros((n, 1, d), dtype=np.float32)
+    k = np.zeros((n, 1, d), dtype=np.float32)
+    q[:, :, :4] = np.repeat(qt, 64, axis=0)
+    k[:, :, :4] = np.repeat(kt, 64, axis=0)
+    qb, kb = si.f32_to_bf16_bits(q), si.f32_to_bf16_bits(k)
+    attn = vd.Attention(n, n, 1, d)
+    tiles = attn.vsa_select(up(qb, dev), up(kb, dev), keep=keep)
+    torch.cuda.synchronize()
+    want = oracle.vsa_select(qb, kb, keep=keep)
+    scores = np.repeat(qt[:, 0], 1, axis=0) @ kt[:, 0].T
+    assert len(np.unique(scores)) < 20   # the test really is about ties
+    assert np.array_equal(tiles.cpu().numpy(), want)
+
+
+def test_selection_n131072_2048_tiles(dev):
+    """The packed RoPE workload's length without RoPE: 2048 key tiles, two heads."""
+    vd = vdm()
+    n, ht, d = 32 * 64 * 64, 2, 128
+    q = si.normal_bf16((n, ht, d), 3060, si.STREAM_Q)
+    k = si.normal_bf16((n, ht, d), 3060, si.STREAM_K)
+    attn = vd.Attention(n, n, ht, d)
+    keep = attn.vsa_keep(0.8)
+    note(f"vsa selection N={n} tiles={attn.k_tiles} keep={keep}")
+    tiles = attn.vsa_select(up(q, dev), up(k, dev), keep=keep)
+    torch.cuda.synchronize()
+    want = oracle.vsa_select(q, k, keep=keep)
+    assert np.array_equal(tiles.cpu().numpy(), want)
+
+
 def test_keep_count_matches_oracle(dev):
     vd = vdm()
     for n, s in ((75600, 0.8), (4096, 0.8), (4096, 0.0), (131072, 0.8), (130, 0.5), (64, 0.9)):
