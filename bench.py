@@ -12,7 +12,9 @@ calls (two sequences per call, as under classifier-free guidance): the same
 self-attention with B = 2, and text cross-attention over all 40 heads with key
 lengths 512 and 226; and the same workload with q.k on int8 per-block codes
 (``qk_int8_*``: nominal TFLOP/s, and the fraction of a roofline that prices q.k
-at the int8 MFMA peak and the weighted sum at the float16 peak).
+at the int8 MFMA peak and the weighted sum at the float16 peak); and block-sparse
+attention over 64-token tiles at sparsity 0.8 (``vsa_*``: selection and fine-stage
+times, TFLOP/s over the kept keys, speed-up of the whole call over the dense step).
 ``roofline`` prices the attention kernel alone against the MI355X dense
 bf16/fp16 MFMA peak, with its duration from HIP events on the launch stream.
 ``cpu_baseline`` times the float64 oracle on a bounded sample of query rows.
@@ -208,6 +210,34 @@ def main() -> int:
     batched["qk_int8_TFLOPs"] = round(flops / (att8 * 1e-3) / 1e12, 1)
     batched["qk_int8_roofline_frac"] = round(t_peak8 / (att8 * 1e-3), 4)
     del a8, ws8, o8
+
+    # block-sparse attention over 64-token tiles at sparsity 0.8: the coarse selection
+    # (tile means, coarse scores, top-k) and the fine stage (v preparation and the
+    # sparse attention kernel). TFLOP/s counts the keys of the kept tiles only.
+    av = vd.Attention(N_TOK, N_TOK, HEADS_TOTAL, D, head_begin=HEAD_BEGIN, head_count=HEAD_COUNT)
+    keep = av.vsa_keep(0.8)
+    wsv = av.new_vsa_workspace(keep, dev)
+    tiles = torch.empty(av.tiles_shape(keep), dtype=torch.int32, device=dev)
+    ov = torch.empty(av.out_shape, dtype=torch.bfloat16, device=dev)
+    sel_ms = time_calls(lambda: av.vsa_select(qd, kd, keep=keep, tiles=tiles, workspace=wsv), 5)
+    att_ms = time_calls(lambda: av.vsa_attend(qd, kd, vdd, tiles=tiles, out=ov, workspace=wsv), 5)
+    fwd_ms = time_calls(lambda: av.vsa_forward(qd, kd, vdd, keep=keep, out=ov, workspace=wsv), 5)
+    tl = tiles.cpu().numpy()
+    rows = np.full(av.q_tiles, 64, dtype=np.int64)
+    rows[-1] = N_TOK - 64 * (av.q_tiles - 1)
+    tail = N_TOK - 64 * (av.k_tiles - 1)
+    keys = keep * 64 - (64 - tail) * (tl == av.k_tiles - 1).sum(axis=-1)   # [heads, query tiles]
+    vsa_flops = 4.0 * D * float((keys * rows[None, :]).sum())
+    batched["vsa_sparsity"] = 0.8
+    batched["vsa_keep_tiles"] = keep
+    batched["vsa_key_tiles"] = av.k_tiles
+    batched["vsa_select_ms"] = round(sel_ms, 4)
+    batched["vsa_attend_ms"] = round(att_ms, 3)
+    batched["vsa_fwd_ms"] = round(fwd_ms, 3)
+    batched["vsa_TFLOPs"] = round(vsa_flops / (att_ms * 1e-3) / 1e12, 1)
+    batched["vsa_frac_of_peak"] = round(vsa_flops / (att_ms * 1e-3) / 1e12 / PEAK_TFLOPS, 4)
+    batched["vsa_speedup_vs_dense"] = round(step_ms / fwd_ms, 2)
+    del av, wsv, tiles, ov
 
     result = {
         "metric": "attention TFLOP/s + % bf16 MFMA peak at N=75600,H=10,d=128 (1 GPU)",
