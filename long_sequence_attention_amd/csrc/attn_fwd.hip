@@ -378,9 +378,11 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   };
   // scores of the next tile with the weights of the held one; leaves the first
   // kR V^T fragments of the products in `vr`
+  // `issue(g)` runs after score product g (the block-sparse mode issues its
+  // direct loads there, one per product)
   auto score_phase = [&](const char* k_read, const char* v_read, const f32x16 (&s_cur)[QB][KH],
                          f32x16 (&s_next)[QB][KH], const float (&ccur)[QB], const float (&mref)[QB],
-                         f16x8 (&vr)[kR], f16x8 (&pf)[QB][2 * KH], f16x2 (&hv)[QB][kPairs]) {
+                         f16x8 (&vr)[kR], f16x8 (&pf)[QB][2 * KH], f16x2 (&hv)[QB][kPairs], auto&& issue) {
     QFrag kr[kR];
     u32x4 bits[QB][2 * KH];
 #pragma unroll
@@ -396,6 +398,7 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
         s_next[qb][kb] = qk_mfma(kr[g % kR], qf[qb][kk], s_next[qb][kb]);
+      issue(g);
       if (g + kR < kNS)
         kr[g % kR] = kfrag(k_read, g + kR);
       else
@@ -534,12 +537,36 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   auto step = [&](int t, char* k_read, char* k_fill, char* v_read, char* v_fill, f32x16 (&s_cur)[QB][KH],
                   f32x16 (&s_next)[QB][KH], const float (&c_cur)[QB], float (&c_next)[QB],
                   const float (&mref)[QB]) {
-    dma_v(t + NST / 2, v_fill);
-    dma_k(t + NST, k_fill);
     f16x8 vr[kR];
     f16x8 pf[QB][2 * KH];
     f16x2 hv[QB][kPairs];
-    score_phase(k_read, v_read, s_cur, s_next, c_cur, mref, vr, pf, hv);
+    if constexpr (SPARSE) {
+      // Four waves stage a whole K/V tile for only 64 queries, so the CU's
+      // texture path is busy for much of a step: issued back to back, the loads
+      // of all waves queue there together and every wave stalls. Here each wave
+      // computes its addresses first and issues one load per score product, K
+      // (needed first, by the next scores) before V^T.
+      static_assert(C::kKDma + C::kVDma <= kNS, "one direct load per score product");
+      const int tk = tile_of(t + NST), tv = tile_of(t + NST / 2);
+      const char* kt = kbytes + (int64_t)tk * kBlockN * krow_bytes;
+      const int lim = kv_len - 1 - tk * kBlockN;
+      const char* vt = vbytes + (int64_t)tv * C::kVTile;
+      const char* ga[C::kKDma + C::kVDma];
+#pragma unroll
+      for (int i = 0; i < C::kKDma; ++i) ga[i] = kt + (uint32_t)(min(kdma_row[i], lim) * krow_bytes + kdma_off[i]);
+#pragma unroll
+      for (int i = 0; i < C::kVDma; ++i) ga[C::kKDma + i] = vt + vdma_off[i];
+      score_phase(k_read, v_read, s_cur, s_next, c_cur, mref, vr, pf, hv, [&](int g) {
+        if (g < C::kKDma)
+          dma16(ga[g], lds_addr(k_fill) + (wave_u * C::kKDma + g) * 1024);
+        else if (g < C::kKDma + C::kVDma)
+          dma16(ga[g], lds_addr(v_fill) + (wave_u * C::kVDma + g - C::kKDma) * 1024);
+      });
+    } else {
+      dma_v(t + NST / 2, v_fill);
+      dma_k(t + NST, k_fill);
+      score_phase(k_read, v_read, s_cur, s_next, c_cur, mref, vr, pf, hv, [](int) {});
+    }
     if (upper) sync();
     product_phase(v_read, vr, pf, hv, s_next);
     mask_tail(t + 1, s_next);
