@@ -540,13 +540,16 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
     f16x8 vr[kR];
     f16x8 pf[QB][2 * KH];
     f16x2 hv[QB][kPairs];
-    if constexpr (SPARSE) {
-      // Four waves stage a whole K/V tile for only 64 queries, so the CU's
-      // texture path is busy for much of a step: issued back to back, the loads
-      // of all waves queue there together and every wave stalls. Here each wave
-      // computes its addresses first and issues one load per score product, K
-      // (needed first, by the next scores) before V^T.
-      static_assert(C::kKDma + C::kVDma <= kNS, "one direct load per score product");
+    if constexpr (NST == 2) {
+      // With two stages (short keys, block-sparse) two workgroups per CU stage
+      // their own K/V tiles, so the CU's texture path is busy for much of a step:
+      // issued back to back, the loads of all waves queue there together and
+      // every wave stalls. Here each wave computes its addresses first and spreads
+      // its loads evenly over the score products, K (needed first, by the next
+      // scores) before V^T.
+      constexpr int kLoads = C::kKDma + C::kVDma;
+      constexpr int kEvery = kNS / kLoads;
+      static_assert(kEvery >= 1 && kEvery * kLoads <= kNS, "at most one direct load per score product");
       const int tk = tile_of(t + NST), tv = tile_of(t + NST / 2);
       const char* kt = kbytes + (int64_t)tk * kBlockN * krow_bytes;
       const int lim = kv_len - 1 - tk * kBlockN;
@@ -557,10 +560,12 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < C::kVDma; ++i) ga[C::kKDma + i] = vt + vdma_off[i];
       score_phase(k_read, v_read, s_cur, s_next, c_cur, mref, vr, pf, hv, [&](int g) {
-        if (g < C::kKDma)
-          dma16(ga[g], lds_addr(k_fill) + (wave_u * C::kKDma + g) * 1024);
-        else if (g < C::kKDma + C::kVDma)
-          dma16(ga[g], lds_addr(v_fill) + (wave_u * C::kVDma + g - C::kKDma) * 1024);
+        if (g % kEvery != 0) return;
+        const int i = g / kEvery;
+        if (i < C::kKDma)
+          dma16(ga[i], lds_addr(k_fill) + (wave_u * C::kKDma + i) * 1024);
+        else if (i < kLoads)
+          dma16(ga[i], lds_addr(v_fill) + (wave_u * C::kVDma + i - C::kKDma) * 1024);
       });
     } else {
       dma_v(t + NST / 2, v_fill);
