@@ -1,10 +1,13 @@
 // Flash-style attention forward for gfx950 (CDNA4), bf16 q/k, fp16 weights and v.
 //
 // Work split: one workgroup = WAVES waves = BLOCK_M = WAVES * QB * 32 queries of one
-// head; it streams all valid keys of that head in tiles of 64 keys. K tiles (row-
-// major, from the input or the rotated-key workspace) and V^T tiles (prepared in
-// the workspace) reach LDS by direct global->LDS loads (global_load_lds_dwordx4)
-// into four K and four V^T stages, issued four (K) and two (V^T) iterations ahead.
+// head (WAVES / 2 * QB * 32 in the block-sparse mode below); it streams all valid
+// keys of that head in tiles of 64 keys. K tiles (row-major, from the input or the
+// rotated-key workspace) and V^T tiles (prepared in the workspace) reach LDS by
+// direct global->LDS loads (global_load_lds_dwordx4): for long key sequences into
+// four K and four V^T stages, issued four (K) and two (V^T) iterations ahead; for
+// short ones and the block-sparse mode into two of each, so that two workgroups
+// share a CU.
 //
 // Per wave and key tile the scores are formed transposed, S^T = K * Q^T, with
 // v_mfma_f32_32x32x16_bf16: the A operand is a 32-key x 16-dim slice of K read
@@ -17,9 +20,9 @@
 // A operand for a lane is one 16-byte LDS read.
 //
 // Per iteration a wave forms the scores of the next tile while it turns the held
-// scores into weights, then runs the weight products. The two waves sharing a
-// SIMD are kept half an iteration apart (one forms scores and weights while the
-// other runs products), so the SIMD's matrix and vector units overlap.
+// scores into weights, then runs the weight products. With four stages the two
+// waves sharing a SIMD are kept half an iteration apart (one forms scores and
+// weights while the other runs products).
 //
 // Block-sparse mode (SPARSE): the workgroup is one 64-query tile and visits only
 // the key tiles listed for it, in list order. Four waves split it: wave w takes

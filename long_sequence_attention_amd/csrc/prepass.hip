@@ -2,6 +2,8 @@
 //   * prepare: v of the head share -> float16 V^T tiles in the workspace (keys
 //     permuted inside groups of 16 to match the weight layout of the attention
 //     kernel, zero past the valid keys), and with RoPE the rotated keys;
+//   * quantize (int8 q.k): symmetric int8 codes and float32 scales of q (128
+//     tokens per block, softmax scale folded in) and k (64 keys per block);
 //   * pack / unpack: [n, Ht, d] <-> [G, n, Ht/G, d] for the Ulysses exchange;
 //   * rope probe: the (t, y, x, band, i) index map as the kernels compute it.
 #include "common.hpp"
