@@ -133,6 +133,24 @@ def test_selection_n131072_2048_tiles(dev):
     assert np.array_equal(tiles.cpu().numpy(), want)
 
 
+@pytest.mark.parametrize("n", [1, 63, 64, 65, 129, 200])
+@pytest.mark.parametrize("d", [64, 128])
+def test_degenerate_and_ragged_sizes(dev, n, d):
+    """One token, one partial tile, exactly one tile, a one-token last tile..., with
+    one kept tile and with all of them."""
+    vd = vdm()
+    q, k, v = inputs(n, 2, d, 3070 + n)
+    attn = vd.Attention(n, n, 2, d)
+    for keep in sorted({1, attn.k_tiles}):
+        out = attn.vsa_forward(up(q, dev), up(k, dev), up(v, dev), keep=keep)
+        tiles = attn.vsa_select(up(q, dev), up(k, dev), keep=keep)
+        torch.cuda.synchronize()
+        want = oracle.vsa_select(q, k, keep=keep)
+        assert np.array_equal(tiles.cpu().numpy(), want), (n, d, keep)
+        ref, _ = oracle.vsa_reference(q, k, v, tiles=want)
+        check(as_f64(out), ref, f"vsa n={n} d={d} keep={keep}")
+
+
 def test_keep_count_matches_oracle(dev):
     vd = vdm()
     for n, s in ((75600, 0.8), (4096, 0.8), (4096, 0.0), (131072, 0.8), (130, 0.5), (64, 0.9)):
