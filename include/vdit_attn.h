@@ -49,7 +49,9 @@
  *     never frees or keeps them past the call;
  *   - pointers passed to compute calls must be 16-byte aligned;
  *   - calls taking `hip_stream` (a hipStream_t; NULL = default stream) only
- *     enqueue work on that stream and never synchronise the host;
+ *     enqueue kernels on that stream: they never allocate, fill memory with the
+ *     runtime or synchronise the host, so they may be captured in a HIP graph
+ *     (scalar arguments such as key_len are then fixed at capture);
  *   - errors come back as vdit_status_t values, never as exceptions or aborts;
  *     a shape or argument error is reported before anything is enqueued;
  *   - the handle is immutable after create: calls on one handle may run on
