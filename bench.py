@@ -14,7 +14,10 @@ lengths 512 and 226; and the same workload with q.k on int8 per-block codes
 (``qk_int8_*``: nominal TFLOP/s, and the fraction of a roofline that prices q.k
 at the int8 MFMA peak and the weighted sum at the float16 peak); and block-sparse
 attention over 64-token tiles at sparsity 0.8 (``vsa_*``: selection and fine-stage
-times, TFLOP/s over the kept keys, speed-up of the whole call over the dense step).
+times, TFLOP/s over the kept keys, speed-up of the whole call over the dense step);
+and the other workloads of the hot path, each timed alone: N=256 H=2 d=64 (latency),
+N=4096 H=10, text cross-attention (75600 queries, 40 heads, 512 keys, key lengths 512 and a
+seeded one), packed [N,3,40,128] with 3D RoPE at N=131072.
 ``roofline`` prices the attention kernel alone against the MI355X dense
 bf16/fp16 MFMA peak, with its duration from HIP events on the launch stream.
 ``cpu_baseline`` times the float64 oracle on a bounded sample of query rows.
@@ -239,6 +242,42 @@ def main() -> int:
     batched["vsa_speedup_vs_dense"] = round(step_ms / fwd_ms, 2)
     del av, wsv, tiles, ov
 
+    # the other workloads of the hot path, each timed alone (prepare + attend); inputs
+    # are slices of this run's tensors, or fresh N(0, sigma^2) bfloat16 draws on the GPU
+    workloads = {}
+
+    def fwd_ms(a, q_, k_, v_, reps, **kw):
+        w_ = a.new_workspace(dev)
+        o_ = torch.empty(a.out_shape, dtype=torch.bfloat16, device=dev)
+        return time_calls(lambda: a.forward(q_, k_, v_, out=o_, workspace=w_, **kw), reps)
+
+    q1, k1, v1 = (t[:256, :2, :64].contiguous() for t in (qd, kd, vdd))
+    ms = fwd_ms(vd.Attention(256, 256, 2, 64), q1, k1, v1, 50)
+    workloads["n256_h2_d64_fwd_us"] = round(ms * 1e3, 1)
+    q2, k2, v2 = (t[:4096, :10].contiguous() for t in (qd, kd, vdd))
+    ms = fwd_ms(vd.Attention(4096, 4096, 10, D), q2, k2, v2, 20)
+    workloads["n4096_h10_fwd_ms"] = round(ms, 4)
+    workloads["n4096_h10_TFLOPs"] = round(4.0 * 4096 * 4096 * D * 10 / (ms * 1e-3) / 1e12, 1)
+    del q1, k1, v1, q2, k2, v2
+    ax1 = vd.Attention(N_TOK, 512, HEADS_TOTAL, D, use_key_mask=True)
+    kx, vx = kd[:512].contiguous(), vdd[:512].contiguous()
+    for L in (512, si.key_length(1004)):
+        ms = fwd_ms(ax1, qd, kx, vx, 10, key_len=L)
+        tag = f"text_cross_n{N_TOK}_h40_L{L}"
+        workloads[f"{tag}_ms"] = round(ms, 4)
+        workloads[f"{tag}_TFLOPs"] = round(4.0 * N_TOK * L * D * HEADS_TOTAL / (ms * 1e-3) / 1e12, 1)
+        workloads[f"{tag}_GBps"] = round((2 * N_TOK + 2 * L) * HEADS_TOTAL * D * 2 / (ms * 1e-3) / 1e9, 1)
+    del ax1, kx, vx
+    n5 = 32 * 64 * 64
+    gen = torch.Generator(device=dev).manual_seed(1005)
+    qkv = (torch.randn((n5, 3, HEADS_TOTAL, D), generator=gen, device=dev) * 0.5).to(torch.bfloat16)
+    a5 = vd.Attention(n5, n5, HEADS_TOTAL, D, layout="N3HD",
+                      rope={"grid": (32, 64, 64), "dims": (44, 42, 42), "base": 10000.0})
+    ms = fwd_ms(a5, qkv, None, None, 2)
+    workloads["packed_rope_n131072_h40_fwd_ms"] = round(ms, 2)
+    workloads["packed_rope_n131072_h40_TFLOPs"] = round(4.0 * n5 * n5 * D * HEADS_TOTAL / (ms * 1e-3) / 1e12, 1)
+    del qkv, a5
+
     result = {
         "metric": "attention TFLOP/s + % bf16 MFMA peak at N=75600,H=10,d=128 (1 GPU)",
         "value": round(value, 2),
@@ -272,6 +311,7 @@ def main() -> int:
             "prepare_GBps": round((2 * N_TOK * HEAD_COUNT * D * 2) / (prep_ms * 1e-3) / 1e9, 1),
             **pack,
             **batched,
+            **workloads,
         },
     }
     if args.cpu_rows > 0:
