@@ -737,11 +737,16 @@ hipError_t launch_attn_fwd(const AttnArgs& a, int head_dim, bool rope_q, bool qk
   if (a.batch <= 0 || a.batch > kMaxBatch || a.hc <= 0) return hipErrorInvalidValue;
   int max_len = 0;
   for (int b = 0; b < a.batch; ++b) max_len = a.kv_len[b] > max_len ? a.kv_len[b] : max_len;
-  const bool small = max_len <= kSmallKeys;
+  const bool short_keys = max_len <= kSmallKeys;
   if (qk_int8) {
+    // the two-stage int8 configuration holds the k scales of short key sequences only
     if (head_dim != 128 || rope_q) return hipErrorInvalidValue;
-    return small ? launch_fwd_t<128, 1, 4, 2, false, true>(a, s) : launch_fwd_t<128, 1, 8, 4, false, true>(a, s);
+    return short_keys ? launch_fwd_t<128, 1, 4, 2, false, true>(a, s) : launch_fwd_t<128, 1, 8, 4, false, true>(a, s);
   }
+  // short keys, or too few 256-query workgroups to give every CU one: the
+  // 128-query configuration, two workgroups per CU
+  const int64_t big_wgs = (int64_t)((a.nq + 255) / 256) * a.hc * a.batch;
+  const bool small = short_keys || big_wgs < 256;
   if (head_dim == 128) {
     if (small)
       return rope_q ? launch_fwd_t<128, 1, 4, 2, true, false>(a, s) : launch_fwd_t<128, 1, 4, 2, false, false>(a, s);
