@@ -182,7 +182,9 @@ def test_explicit_scale(dev):
 
 
 @pytest.mark.parametrize("grid,dims,d", [((3, 5, 7), (44, 42, 42), 128), ((4, 4, 16), (24, 20, 20), 64),
-                                         ((1, 1, 300), (44, 42, 42), 128)])
+                                         ((1, 1, 300), (44, 42, 42), 128),
+                                         # more than 1024 keys on a small grid (two-stage kernel)
+                                         ((4, 16, 40), (44, 42, 42), 128), ((3, 20, 30), (24, 20, 20), 64)])
 def test_rope_small_grids(dev, grid, dims, d):
     vd = vdm()
     n = grid[0] * grid[1] * grid[2]
