@@ -698,23 +698,51 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
     }
   }
 
-  // ---- epilogue: normalise, round to bf16, store [nq, hc, d]
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float lt = KS == 2 ? l_run[qb] : l_run[qb] + __shfl_xor(l_run[qb], 32);
+  // ---- epilogue: normalise, round to bf16 and store [nq, hc, d]. Each wave stages
+  // its 32 rows in LDS (the staging buffers are free now: every wave has passed the
+  // last barrier after its last read of them) and writes them back as whole rows, 16
+  // bytes per lane: one store instruction covers 64 / (D / 8) contiguous rows instead
+  // of 16-byte pieces of 32 rows. Within a row the 16-byte granules are permuted by
+  // an XOR with the row index, so that the writes of the accumulator layout spread
+  // over the LDS banks.
+  static_assert(QB == 1, "one 32-query block per wave");
+  constexpr int kRowBytes = D * 2;
+  constexpr int kGran = D / 8;               // 16-byte granules per row
+  constexpr int kRowsPerStore = kWave / kGran;
+  char* stg;
+  if constexpr (KS == 2) {
+    stg = qw == 0 ? k_st0 : v_st0;           // this query block's merge buffer
+  } else {
+    const int pair = wave_u >> 1;
+    char* arr = pair == 0 ? v_st0 : pair == 1 ? v_st1 : pair == 2 ? v_st2 : v_st3;
+    stg = arr + (wave_u & 1) * 32 * kRowBytes;
+  }
+  {
+    const float lt = KS == 2 ? l_run[0] : l_run[0] + __shfl_xor(l_run[0], 32);
     const float inv = 1.0f / lt;
-    const int qi = q0 + qb * 32 + l32;
-    if (qi < a.nq) {
-      __bf16* op = a.out + bat * a.out_batch + ((int64_t)qi * a.hc + head) * D + 4 * hl;
+    const int swz = 2 * (l32 & (kGran - 1));
 #pragma unroll
-      for (int db = 0; db < C::kDB; ++db)
+    for (int db = 0; db < C::kDB; ++db)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          bf16x4 w;
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 w;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[qb][db][4 * g + e] * inv);
-          *reinterpret_cast<bf16x4*>(op + db * 32 + 8 * g) = w;
-        }
+        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[0][db][4 * g + e] * inv);
+        const int c = db * 8 + 2 * g + hl;     // 8-byte piece of the row
+        *reinterpret_cast<bf16x4*>(stg + l32 * kRowBytes + ((c ^ swz) << 3)) = w;
+      }
+  }
+  {
+    const int gi = lane % kGran;
+#pragma unroll
+    for (int k = 0; k < 32 / kRowsPerStore; ++k) {
+      const int row = k * kRowsPerStore + lane / kGran;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stg + row * kRowBytes + (((2 * gi) ^ (2 * (row & (kGran - 1)))) << 3));
+      const int qi = q0 + row;
+      if (qi < a.nq) {
+        __bf16* op = a.out + bat * a.out_batch + ((int64_t)qi * a.hc + head) * D + gi * 8;
+        *reinterpret_cast<u32x4*>(op) = v;
+      }
     }
   }
 }
