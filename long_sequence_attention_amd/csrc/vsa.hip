@@ -27,9 +27,25 @@ __global__ void __launch_bounds__(64) vsa_mean_kernel(VsaMeanArgs a) {
   float s[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) s[e] = 0.0f;
-  for (int r = 0; r < cnt; ++r) {
+  if (cnt == 64) {
+    // full tile: all 64 loads in flight in groups of 16, the sums still in token order
 #pragma unroll
-    for (int e = 0; e < E; ++e) s[e] = __fadd_rn(s[e], (float)p[(int64_t)r * a.row + e]);
+    for (int r0 = 0; r0 < 64; r0 += 16) {
+      __bf16 x[16][E];
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+#pragma unroll
+        for (int e = 0; e < E; ++e) x[r][e] = p[(int64_t)(r0 + r) * a.row + e];
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+#pragma unroll
+        for (int e = 0; e < E; ++e) s[e] = __fadd_rn(s[e], (float)x[r][e]);
+    }
+  } else {
+    for (int r = 0; r < cnt; ++r) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) s[e] = __fadd_rn(s[e], (float)p[(int64_t)r * a.row + e]);
+    }
   }
   float* m = a.mean + ((int64_t)bh * a.tiles + t) * D + threadIdx.x * E;
 #pragma unroll
