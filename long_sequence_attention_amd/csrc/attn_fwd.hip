@@ -706,6 +706,9 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   // an XOR with the row index, so that the writes of the accumulator layout spread
   // over the LDS banks.
   static_assert(QB == 1, "one 32-query block per wave");
+  // two waves' rows per full-size V^T stage: stages 2 and 3 exist only with NST = 4
+  static_assert(KS == 2 || WAVES <= (NST == 4 ? 8 : 4), "epilogue staging needs two waves per V^T stage");
+  static_assert(32 * D * 2 * 2 <= C::kVTile, "two waves' rows fit one V^T stage");
   constexpr int kRowBytes = D * 2;
   constexpr int kGran = D / 8;               // 16-byte granules per row
   constexpr int kRowsPerStore = kWave / kGran;
