@@ -392,8 +392,59 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int kb = 0; kb < KH; ++kb) s_next[qb][kb] = f32x16{};
+    // The weights of a pair p take three dependent steps: x = s*c - m (fma), 2^x
+    // (v_exp_f32, on the transcendental unit), rounding to float16. They are spread
+    // over three consecutive products: group g rounds the pair of group g-1, takes
+    // 2^x for its own pair and forms x for the pair of group g+1, so the steps in
+    // one group are independent and the transcendental unit works alongside the
+    // other vector instructions (which it does; one chained group let them take
+    // turns).
+    float xs[kPPG][QB][2], es[kPPG][QB][2];
+    auto form_x = [&](int g) {
+#pragma unroll
+      for (int j = 0; j < kPPG; ++j) {
+        const int p = g * kPPG + j;
+        const int s4 = p >> 2, e = p & 3;
+        const int skb = s4 >> 1, r = (s4 & 1) * 8 + 2 * e;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const float nm = -mref[qb];
+          xs[j][qb][0] = __builtin_fmaf(s_cur[qb][skb][r], ccur[qb], nm);
+          xs[j][qb][1] = __builtin_fmaf(s_cur[qb][skb][r + 1], ccur[qb], nm);
+          asm volatile("" : "+v"(xs[j][qb][0]), "+v"(xs[j][qb][1]));  // keeps x in its group
+        }
+      }
+    };
+    auto exp_x = [&]() {
+#pragma unroll
+      for (int j = 0; j < kPPG; ++j)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          es[j][qb][0] = __builtin_amdgcn_exp2f(xs[j][qb][0]);
+          es[j][qb][1] = __builtin_amdgcn_exp2f(xs[j][qb][1]);
+          asm volatile("" : "+v"(es[j][qb][0]), "+v"(es[j][qb][1]));  // keeps 2^x in its group
+        }
+    };
+    auto round_w = [&](int g) {
+#pragma unroll
+      for (int j = 0; j < kPPG; ++j) {
+        const int p = g * kPPG + j;
+        const int s4 = p >> 2, e = p & 3;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          f16x2 h2;
+          h2[0] = (_Float16)es[j][qb][0];
+          h2[1] = (_Float16)es[j][qb][1];
+          uint32_t u = __builtin_bit_cast(uint32_t, h2);
+          asm volatile("" : "+v"(u));  // keeps the weights in this group
+          hv[qb][p] = __builtin_bit_cast(f16x2, u);
+          bits[qb][s4][e] = u;
+        }
+      }
+    };
 #pragma unroll
     for (int j = 0; j < kR; ++j) kr[j] = kfrag(k_read, j);
+    form_x(0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int g = 0; g < kNS; ++g) {
@@ -406,24 +457,12 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
         kr[g % kR] = kfrag(k_read, g + kR);
       else
         vr[g + kR - kNS] = vfrag(v_read, g + kR - kNS);
-#pragma unroll
-      for (int p = g * kPPG; p < (g + 1) * kPPG; ++p) {
-        const int s4 = p >> 2, e = p & 3;
-        const int skb = s4 >> 1, r = (s4 & 1) * 8 + 2 * e;
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const float nm = -mref[qb];
-          f16x2 h2;
-          h2[0] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[qb][skb][r], ccur[qb], nm));
-          h2[1] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[qb][skb][r + 1], ccur[qb], nm));
-          uint32_t u = __builtin_bit_cast(uint32_t, h2);
-          asm volatile("" : "+v"(u));  // keeps the weights in this group
-          hv[qb][p] = __builtin_bit_cast(f16x2, u);
-          bits[qb][s4][e] = u;
-        }
-      }
+      if (g > 0) round_w(g - 1);
+      exp_x();
+      if (g + 1 < kNS) form_x(g + 1);
       __builtin_amdgcn_sched_barrier(0);
     }
+    round_w(kNS - 1);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
