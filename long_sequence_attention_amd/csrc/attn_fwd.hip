@@ -277,6 +277,17 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
     for (int s4 = 0; s4 < 2 * KH; ++s4) voff[s4] = l32 * C::kVRow + (((2 * (s4 + 2 * kblk0) + hl) ^ vswz) << 4);
   }
+  // V^T reads address the lowest V^T stage plus the lane's offset, held opaque, so
+  // that each read is that register plus an immediate (stage and 32-row block, below
+  // 64 KB); folded into one constant the stage base exceeds the 16-bit immediate
+  // and costs an OR per read
+  const uint32_t v_lo = min(min(lds_addr(v_st0), lds_addr(v_st1)), min(lds_addr(v_st2), lds_addr(v_st3)));
+  uint32_t vbase[2 * KH];
+#pragma unroll
+  for (int s4 = 0; s4 < 2 * KH; ++s4) {
+    vbase[s4] = v_lo + voff[s4];
+    asm volatile("" : "+v"(vbase[s4]));
+  }
 
   // S^T = K * Q^T for the K tile in `kl`
   // one q.k product: bfloat16, or int8 with the int32 accumulator carried in the
@@ -321,17 +332,19 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
     const bool last = SPARSE ? t < ntiles && tile_of(t) == ktiles - 1 : t == ntiles - 1;
     if (last && ragged) {
       if constexpr (SPARSE) t = tile_of(t);
-      // keeps the compiler from executing this block unconditionally with selects
-      asm volatile("");
+      // the lane's first key offset past the valid keys of the tile; opaque, so the
+      // compiler neither executes this block unconditionally with selects nor keeps
+      // the 32 comparisons of the last tile alive across the loop (64 scalar
+      // registers, which it then spills)
+      int lim = kv_len - t * kBlockN - kblk0 * 32 - 4 * hl;
+      asm volatile("" : "+v"(lim));
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int kb = 0; kb < KH; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = t * kBlockN + (kb + kblk0) * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-            if (key >= kv_len) s[qb][kb][r] = -__builtin_inff();
-          }
+          for (int r = 0; r < 16; ++r)
+            if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) s[qb][kb][r] = -__builtin_inff();
     }
   };
   // maximum of the scores of each query in the tile (both lane halves), times c
@@ -377,7 +390,8 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
     return *reinterpret_cast<const QFrag*>(kl + (j % KH + kblk0) * 32 * C::kKRow + koff[j / KH]);
   };
   auto vfrag = [&](const char* vl, int j) {
-    return *reinterpret_cast<const f16x8*>(vl + (j % C::kDB) * 32 * C::kVRow + voff[j / C::kDB]);
+    const uint32_t addr = vbase[j / C::kDB] + (lds_addr(vl) - v_lo) + (j % C::kDB) * 32 * C::kVRow;
+    return *(const __attribute__((address_space(3))) f16x8*)(uintptr_t)addr;
   };
   // scores of the next tile with the weights of the held one; leaves the first
   // kR V^T fragments of the products in `vr`
