@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libvdit_attn.so")
-SOURCES = ["attn_fwd.hip", "prepass.hip", "vsa.hip", "api.hip"]
+SOURCES = ["attn_fwd.hip", "attn_resident.hip", "prepass.hip", "vsa.hip", "api.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -35,7 +35,7 @@ def hipcc() -> str:
 # Kernels whose registers must never spill to scratch memory: an outlined helper
 # or a spill moves their score and accumulator arrays into scratch and costs an
 # order of magnitude, with correct results, so the build rejects it.
-NO_SCRATCH_SOURCES = ["attn_fwd.hip", "prepass.hip", "vsa.hip"]
+NO_SCRATCH_SOURCES = ["attn_fwd.hip", "attn_resident.hip", "prepass.hip", "vsa.hip"]
 
 
 def _scratch_users(asm: str) -> list[str]:

@@ -38,44 +38,12 @@
 // then recomputes its rows with the exact row maximum. The row sum is taken from
 // the rounded float16 weights (v_dot2), the same values the product uses.
 #include "common.hpp"
+#include "lds.hpp"
+
+#include <atomic>
 
 namespace vdit {
 namespace {
-
-// 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4):
-// lane l of the wave writes LDS bytes [lds + 16 l, lds + 16 l + 16); `lds` is an
-// LDS byte address, the same for the whole wave. Written as inline assembly so
-// that the compiler does not track these loads: every wait for them is explicit
-// (wait_vm), which lets loads for later tiles stay in flight across barriers.
-// The statement has no register outputs; the LDS address is an M0 input.
-// Because the compiler does not see a memory instruction here, it also does not
-// insert the wait states such an instruction needs after its operands are
-// written: the global address therefore comes in VGPRs (dependencies on VGPRs
-// are interlocked by the hardware, unlike an SGPR base written by VALU), and
-// the s_nop covers the one wait state an LDS-DMA load needs after M0 is written.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
-}
-
-// s_waitcnt vmcnt(N): all but the newest N vector-memory loads of this wave have
-// completed (loads complete in issue order).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-// workgroup barrier that the compiler may not move LDS accesses across; it
-// waits for nothing by itself
-__device__ __forceinline__ void barrier_only() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const char* p) {
-  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
-}
 
 template <int D, int QB, int WAVES, bool QK8 = false, int KS = 1>
 struct FwdCfg {
@@ -814,6 +782,22 @@ hipError_t launch_fwd_t(AttnArgs a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// compute units of the current device, queried once per device
+int device_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int v = cached[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < kMaxDevices) cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 }  // namespace
 
 
@@ -826,6 +810,12 @@ hipError_t launch_attn_fwd(const AttnArgs& a, int head_dim, bool rope_q, bool qk
     // the two-stage int8 configuration holds the k scales of short key sequences only
     if (head_dim != 128 || rope_q) return hipErrorInvalidValue;
     return short_keys ? launch_fwd_t<128, 1, 4, 2, false, true>(a, s) : launch_fwd_t<128, 1, 8, 4, false, true>(a, s);
+  }
+  // keys and values that fit in LDS, with a query tile for every CU: the resident
+  // kernel (one staging of K/V^T per head and workgroup)
+  if (!rope_q && max_len <= resident_max_keys(head_dim)) {
+    const int cus = device_cus();
+    if (cus > 0 && resident_query_tiles(a.nq) * a.hc * a.batch >= cus) return launch_attn_resident(a, head_dim, cus, s);
   }
   // short keys, or too few 256-query workgroups to give every CU one: the
   // 128-query configuration, two workgroups per CU

@@ -207,6 +207,12 @@ struct VsaSelectArgs {
 // Host-side launchers (defined in the kernel translation units).
 hipError_t launch_attn_fwd(const AttnArgs& a, int head_dim, bool rope_q, bool qk_int8, hipStream_t s);
 hipError_t launch_attn_sparse(const AttnArgs& a, int head_dim, hipStream_t s);
+// Keys and values resident in LDS (short key sequences): the longest key length
+// it takes for a head dimension (0 if none), its query tiles per head, and the
+// launch on a persistent grid of at most `cus` workgroups.
+int resident_max_keys(int head_dim);
+int64_t resident_query_tiles(int32_t nq);
+hipError_t launch_attn_resident(const AttnArgs& a, int head_dim, int cus, hipStream_t s);
 hipError_t launch_vsa_means(const VsaMeanArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_vsa_select(const VsaSelectArgs& a, hipStream_t s);
 hipError_t launch_prepare(const PrepArgs& a, int head_dim, bool rope_k, hipStream_t s);
