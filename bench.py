@@ -43,7 +43,8 @@ PEAK_TFLOPS = 2500.0          # MI355X dense bf16 / fp16 MFMA
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 PEAK_INT8_TOPS = 5000.0       # MI355X dense int8 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_n75600_h10_traffic.json")
-KERNEL_SOURCES = ["long_sequence_attention_amd/csrc/attn_fwd.hip", "long_sequence_attention_amd/csrc/common.hpp"]
+KERNEL_SOURCES = ["long_sequence_attention_amd/csrc/attn_fwd.hip", "long_sequence_attention_amd/csrc/lds.hpp",
+                  "long_sequence_attention_amd/csrc/common.hpp"]
 
 
 def kernel_source_hash() -> str:

@@ -129,13 +129,15 @@ __global__ void __launch_bounds__(kResThreads) attn_resident_kernel(AttnArgs a, 
   // ---- q of this wave's 32 rows of query tile `it` into the B-operand registers;
   // rows past nq read row nq - 1 (their outputs are not stored)
   bf16x8 qf[C::kDK];
-  auto load_q = [&](int it) {
+  auto q_addr = [&](int it) {
     const int bh = it / a.n_qtiles;
     const int qt = it - bh * a.n_qtiles;
     const int bat = bh / a.hc;
     const int head = bh - bat * a.hc;
     const int qi = min(qt * kResQ + wave * 32 + l32, a.nq - 1);
-    const __bf16* qp = a.q + bat * a.q_batch + (int64_t)qi * a.q_row + (int64_t)head * a.q_head + 8 * hl;
+    return a.q + bat * a.q_batch + (int64_t)qi * a.q_row + (int64_t)head * a.q_head + 8 * hl;
+  };
+  auto load_q = [&](const __bf16* qp) {
 #pragma unroll
     for (int kk = 0; kk < C::kDK; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qp + 16 * kk);
   };
@@ -293,10 +295,10 @@ __global__ void __launch_bounds__(kResThreads) attn_resident_kernel(AttnArgs a, 
   // s[0]. Every tile but the last of the array forms the scores of the next array
   // tile, also past ntiles (stale LDS, never used: one tile of discarded products
   // per query tile when the keys do not fill the array, where the kernel waits on
-  // memory anyway), so each tile has a single code path. With `next` >= 0 the q of
-  // query tile `next` is loaded right after the last score product that runs.
+  // memory anyway), so each tile has a single code path. With `qnext` set, the q
+  // rows it points to are loaded right after the last score product that runs.
   f32x16 s[2][2];
-  auto main_pass = [&](float mref, int next) {
+  auto main_pass = [&](float mref, const __bf16* qnext) {
     l_run = 0.0f;
 #pragma unroll
     for (int db = 0; db < C::kDB; ++db) o[db] = f32x16{};
@@ -311,7 +313,7 @@ __global__ void __launch_bounds__(kResThreads) attn_resident_kernel(AttnArgs a, 
           const std::integral_constant<int, T + 1> nxt{};
           score_phase(nxt, s[T & 1], s[(T + 1) & 1], mref, vr, pf, hv);
           mask_last(nxt, s[(T + 1) & 1]);
-          if (T == last_scores && next >= 0) load_q(next);
+          if (T == last_scores && qnext) load_q(qnext);
         } else {
           weight_phase(T_, s[T & 1], mref, vr, pf, hv);
         }
@@ -322,7 +324,7 @@ __global__ void __launch_bounds__(kResThreads) attn_resident_kernel(AttnArgs a, 
 
   const std::integral_constant<int, 0> tile0{};
   int cur_bh = -1;
-  if (it0 < it1) load_q(it0);
+  if (it0 < it1) load_q(q_addr(it0));
   for (int it = it0; it < it1; ++it) {
     const int bh = it / a.n_qtiles;
     const int qt = it - bh * a.n_qtiles;
@@ -354,7 +356,7 @@ __global__ void __launch_bounds__(kResThreads) attn_resident_kernel(AttnArgs a, 
       wait_vm<0>();
       barrier_only();
     }
-    const int next = it + 1 < it1 ? it + 1 : -1;
+    const __bf16* qnext = it + 1 < it1 ? q_addr(it + 1) : nullptr;
 
     // reference: the maximum of each row over the first key tile. Rare second
     // attempt: a weight left the float16 range (or the inputs were not finite), and
@@ -363,12 +365,12 @@ __global__ void __launch_bounds__(kResThreads) attn_resident_kernel(AttnArgs a, 
     mask_last(tile0, s[0]);
     float mref = tile_max(s[0]);
     for (int attempt = 0;; ++attempt) {
-      main_pass(mref, attempt == 0 ? next : -1);
+      main_pass(mref, attempt == 0 ? qnext : nullptr);
       if (attempt == 1 || !__any(!__builtin_isfinite(l_run))) {
-        if (attempt == 1 && next >= 0) load_q(next);
+        if (attempt == 1 && qnext) load_q(qnext);
         break;
       }
-      load_q(it);
+      load_q(q_addr(it));
       float mx = -__builtin_inff();
       static_for<0, C::kMaxTiles>([&](auto T_) {
         if (decltype(T_)::value < ntiles) {
