@@ -32,8 +32,8 @@
  *
  * Numerics: q.k products in bfloat16 with float32 accumulation; softmax in
  * float32, taken relative to a fixed per-row reference (the maximum over the
- * first 64 keys; the workgroup recomputes its rows with the exact maximum if a
- * weight would leave the float16 range); the weights are rounded to float16 and
+ * first 64 keys; rows are recomputed with the exact maximum if a weight would
+ * leave the float16 range); the weights are rounded to float16 and
  * v is converted once to float16 for the weighted sum (float32 accumulation);
  * the output is rounded to bfloat16 (nearest even). v values must lie within the
  * float16 range (|v| <= 65504).
