@@ -69,10 +69,9 @@ struct FwdCfg {
 // V^T one iteration ahead, 64 KB of LDS) so that two smaller workgroups share a
 // CU and one computes while the other waits on memory.
 // QK8: q.k on int8 codes per block (v_mfma_i32_32x32x32_i8), prepared by the
-// quantize pre-pass with the softmax scale folded into q. The integer scores of
-// the next tile are converted to float during the weight products; each tile's
-// weights then use c = q scale * k scale * log2 e per lane, so the softmax costs
-// one conversion per score more than with bfloat16 q.k.
+// quantize pre-pass with the softmax scale folded into q. The integer scores come
+// out of the products already readable as floats (offset by a constant, see
+// qk_mfma); each tile's weights use c = q scale * k scale * log2 e per lane.
 template <int D, int QB, int WAVES, int NST, bool ROPE, bool QK8, bool SPARSE>
 __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   constexpr int KS = SPARSE ? 2 : 1;  // waves per query block (key split)
@@ -259,7 +258,15 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
 
   // S^T = K * Q^T for the K tile in `kl`
   // one q.k product: bfloat16, or int8 with the int32 accumulator carried in the
-  // bits of the float vector until it is converted
+  // bits of the float vector. The int8 accumulators start from the bits of
+  // kMagic = 1.5 * 2^23, so that a finished accumulator holding kMagic's bits + s
+  // (|s| <= 128 * 127 * 127 < 2^22) reads as the float kMagic + s exactly: no
+  // conversion; the weights subtract kMagic * c with the reference, and the tile
+  // maximum subtracts kMagic (exactly) before it is scaled.
+  constexpr float kMagic = 12582912.0f;
+  f32x16 acc0;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc0[r] = QK8 ? kMagic : 0.0f;
   auto qk_mfma = [](const QFrag& ka, const QFrag& qv, f32x16 acc) -> f32x16 {
     if constexpr (QK8)
       return __builtin_bit_cast(
@@ -271,7 +278,7 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int kb = 0; kb < KH; ++kb) s[qb][kb] = f32x16{};
+      for (int kb = 0; kb < KH; ++kb) s[qb][kb] = acc0;
 #pragma unroll
     for (int kk = 0; kk < C::kDK; ++kk) {
 #pragma unroll
@@ -280,18 +287,6 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) s[qb][kb] = qk_mfma(ka, qf[qb][kk], s[qb][kb]);
       }
-    }
-    if constexpr (QK8) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int kb = 0; kb < KH; ++kb) {
-          const i32x16 iv = __builtin_bit_cast(i32x16, s[qb][kb]);
-          f32x16 fv;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) fv[r] = (float)iv[r];
-          s[qb][kb] = fv;
-        }
     }
   };
   // scores of keys past kv_len to -inf (only the last key tile can hold such keys)
@@ -327,6 +322,7 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
+      if constexpr (QK8) mx -= kMagic;
       m[qb] = mx * ct[qb];
     }
   };
@@ -373,7 +369,7 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int kb = 0; kb < KH; ++kb) s_next[qb][kb] = f32x16{};
+      for (int kb = 0; kb < KH; ++kb) s_next[qb][kb] = acc0;
     // The weights of a pair p take three dependent steps: x = s*c - m (fma), 2^x
     // (v_exp_f32, on the transcendental unit), rounding to float16. They are spread
     // over three consecutive products: group g rounds the pair of group g-1, takes
@@ -390,7 +386,7 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
         const int skb = s4 >> 1, r = (s4 & 1) * 8 + 2 * e;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-          const float nm = -mref[qb];
+          const float nm = QK8 ? -__builtin_fmaf(kMagic, ccur[qb], mref[qb]) : -mref[qb];
           xs[j][qb][0] = __builtin_fmaf(s_cur[qb][skb][r], ccur[qb], nm);
           xs[j][qb][1] = __builtin_fmaf(s_cur[qb][skb][r + 1], ccur[qb], nm);
           asm volatile("" : "+v"(xs[j][qb][0]), "+v"(xs[j][qb][1]));  // keeps x in its group
@@ -475,18 +471,6 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
           lsum[qb][p >> 2] = __builtin_amdgcn_fdot2(hv[qb][p], ones, lsum[qb][p >> 2], false);
           asm volatile("" : "+v"(lsum[qb][p >> 2]));  // keeps the sum in this group
         }
-      if constexpr (QK8) {
-        static_assert(32 % kNP == 0, "conversions per product");
-#pragma unroll
-        for (int e = g * (32 / kNP); e < (g + 1) * (32 / kNP); ++e)
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
-            const i32x16 iv = __builtin_bit_cast(i32x16, s_next[qb][e >> 4]);
-            float f = (float)iv[e & 15];
-            asm volatile("" : "+v"(f));  // keeps the conversion in this group
-            s_next[qb][e >> 4][e & 15] = f;
-          }
-      }
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
