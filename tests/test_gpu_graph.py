@@ -99,3 +99,25 @@ def test_block_sparse_graph_replay(dev):
         torch.cuda.synchronize()
         return down(o)
     replay_checks(g, out, eager, q, q_new)
+
+
+def test_resident_cross_attention_graph_replay(dev):
+    # short text keys with query tiles for every CU: the keys-resident kernel (its
+    # persistent grid is sized at capture)
+    import long_sequence_attention_amd as vd
+    nq, nk, ht, d, L = 12000, 256, 8, 128, 200
+    note(f"graph replay resident cross-attention nq={nq} nk={nk} L={L}")
+    q = up(si.normal_bf16((nq, ht, d), 4420, si.STREAM_Q), dev)
+    k = up(si.normal_bf16((nk, ht, d), 4420, si.STREAM_K), dev)
+    v = up(si.normal_bf16((nk, ht, d), 4420, si.STREAM_V), dev)
+    q_new = up(si.normal_bf16((nq, ht, d), 4421, si.STREAM_Q), dev)
+    attn = vd.Attention(nq, nk, ht, d, use_key_mask=True)
+    out = torch.empty(attn.out_shape, dtype=torch.bfloat16, device=dev)
+    ws = attn.new_workspace(dev)
+    g = capture(lambda: attn.forward(q, k, v, key_len=L, out=out, workspace=ws))
+
+    def eager():
+        o = attn.forward(q, k, v, key_len=L)
+        torch.cuda.synchronize()
+        return down(o)
+    replay_checks(g, out, eager, q, q_new)
