@@ -215,14 +215,23 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   // K rows past kv_len re-read the last valid row (their scores are masked), so
   // no row at or beyond kv_len is ever read; tiles past the last one re-read it.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  // byte offsets of the lanes' K chunks inside a full tile (rows unclamped)
+  uint32_t kdma_full[C::kKDma];
+#pragma unroll
+  for (int i = 0; i < C::kKDma; ++i) kdma_full[i] = (uint32_t)(kdma_row[i] * krow_bytes + kdma_off[i]);
   auto dma_k = [&](int t, const char* st) {
     t = tile_of(t);
     const char* kt = kbytes + (int64_t)t * kBlockN * krow_bytes;
     const int lim = kv_len - 1 - t * kBlockN;
+    if (lim >= kBlockN - 1) {
 #pragma unroll
-    for (int i = 0; i < C::kKDma; ++i) {
-      const int row = min(kdma_row[i], lim);
-      dma16(kt + (uint32_t)(row * krow_bytes + kdma_off[i]), lds_addr(st) + (wave_u * C::kKDma + i) * 1024);
+      for (int i = 0; i < C::kKDma; ++i) dma16(kt + kdma_full[i], lds_addr(st) + (wave_u * C::kKDma + i) * 1024);
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::kKDma; ++i) {
+        const int row = min(kdma_row[i], lim);
+        dma16(kt + (uint32_t)(row * krow_bytes + kdma_off[i]), lds_addr(st) + (wave_u * C::kKDma + i) * 1024);
+      }
     }
   };
   auto dma_v = [&](int t, const char* st) {
@@ -330,6 +339,9 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   // O^T accumulators and row sums of the weights
   f32x16 o[QB][C::kDB];
   float l_run[QB];
+  // row sums of the rounded weights, one partial per 16-key group of a tile,
+  // accumulated over the whole pass and added up at its end
+  float lpart[QB][2 * KH];
   const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 
   // ---- one iteration's matrix and vector work, scheduled by hand. A tile has
@@ -446,17 +458,12 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int s4 = 0; s4 < 2 * KH; ++s4) pf[qb][s4] = __builtin_bit_cast(f16x8, bits[qb][s4]);
   };
-  // O^T += V^T P^T; the row sums of the rounded weights (v_dot2) ride along with
-  // the products, which have no other vector work
+  // O^T += V^T P^T; the row sums of the rounded weights (v_dot2 into lpart) ride
+  // along with the products, which have no other vector work
   // with int8 q.k this also converts the integer scores of the next tile to
   // float, two per product
   auto product_phase = [&](const char* v_read, f16x8 (&vr)[kR], const f16x8 (&pf)[QB][2 * KH],
                            const f16x2 (&hv)[QB][kPairs], f32x16 (&s_next)[QB][KH]) {
-    float lsum[QB][2 * KH];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int s4 = 0; s4 < 2 * KH; ++s4) lsum[qb][s4] = 0.0f;
 #pragma unroll
     for (int g = 0; g < kNP; ++g) {
       const int s4 = g / C::kDB, db = g % C::kDB;
@@ -468,17 +475,10 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
       for (int p = g * kPairs / kNP; p < (g + 1) * kPairs / kNP; ++p)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-          lsum[qb][p >> 2] = __builtin_amdgcn_fdot2(hv[qb][p], ones, lsum[qb][p >> 2], false);
-          asm volatile("" : "+v"(lsum[qb][p >> 2]));  // keeps the sum in this group
+          lpart[qb][p >> 2] = __builtin_amdgcn_fdot2(hv[qb][p], ones, lpart[qb][p >> 2], false);
+          asm volatile("" : "+v"(lpart[qb][p >> 2]));  // keeps the sum in this group
         }
       __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      if constexpr (KH == 2)
-        l_run[qb] += (lsum[qb][0] + lsum[qb][1]) + (lsum[qb][2] + lsum[qb][3]);
-      else
-        l_run[qb] += lsum[qb][0] + lsum[qb][1];
     }
   };
 
@@ -589,7 +589,8 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   auto main_pass = [&](const float (&mref)[QB]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      l_run[qb] = 0.0f;
+#pragma unroll
+      for (int s4 = 0; s4 < 2 * KH; ++s4) lpart[qb][s4] = 0.0f;
 #pragma unroll
       for (int db = 0; db < C::kDB; ++db) o[qb][db] = f32x16{};
     }
@@ -609,6 +610,13 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
     // drain the direct loads still in flight before the stages are reused
     wait_vm<0>();
     barrier_only();
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      if constexpr (KH == 2)
+        l_run[qb] = (lpart[qb][0] + lpart[qb][1]) + (lpart[qb][2] + lpart[qb][3]);
+      else
+        l_run[qb] = lpart[qb][0] + lpart[qb][1];
+    }
   };
 
   // ---- reference maximum from the first key tile

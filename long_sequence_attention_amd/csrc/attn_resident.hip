@@ -180,6 +180,7 @@ __global__ void __launch_bounds__(kResThreads) attn_resident_kernel(AttnArgs a, 
 
   f32x16 o[C::kDB];
   float l_run;
+  float lpart[4];  // row sums per 16-key group of a tile, over the whole pass
   const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
   constexpr int kNS = 2 * C::kDK;     // score products per tile
   constexpr int kNP = 4 * C::kDB;     // weight products per tile
@@ -275,7 +276,6 @@ __global__ void __launch_bounds__(kResThreads) attn_resident_kernel(AttnArgs a, 
   };
   // O^T += V^T P^T of tile T, the row sums of the rounded weights alongside
   auto product_phase = [&](auto T_, f16x8 (&vr)[kR], const f16x8 (&pf)[4], const f16x2 (&hv)[kPairs]) {
-    float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int g = 0; g < kNP; ++g) {
       const int s4 = g / C::kDB, db = g % C::kDB;
@@ -283,12 +283,11 @@ __global__ void __launch_bounds__(kResThreads) attn_resident_kernel(AttnArgs a, 
       if (g + kR < kNP) vr[g % kR] = vfrag(T_, g + kR);
 #pragma unroll
       for (int p = g * kPairs / kNP; p < (g + 1) * kPairs / kNP; ++p) {
-        lsum[p >> 2] = __builtin_amdgcn_fdot2(hv[p], ones, lsum[p >> 2], false);
-        asm volatile("" : "+v"(lsum[p >> 2]));
+        lpart[p >> 2] = __builtin_amdgcn_fdot2(hv[p], ones, lpart[p >> 2], false);
+        asm volatile("" : "+v"(lpart[p >> 2]));
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    l_run += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
   };
 
   // one pass over the key tiles with reference mref; the scores of tile 0 are in
@@ -299,7 +298,8 @@ __global__ void __launch_bounds__(kResThreads) attn_resident_kernel(AttnArgs a, 
   // rows it points to are loaded right after the last score product that runs.
   f32x16 s[2][2];
   auto main_pass = [&](float mref, const __bf16* qnext) {
-    l_run = 0.0f;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) lpart[s4] = 0.0f;
 #pragma unroll
     for (int db = 0; db < C::kDB; ++db) o[db] = f32x16{};
     const int last_scores = ntiles == C::kMaxTiles ? ntiles - 2 : ntiles - 1;
@@ -320,6 +320,7 @@ __global__ void __launch_bounds__(kResThreads) attn_resident_kernel(AttnArgs a, 
         product_phase(T_, vr, pf, hv);
       }
     });
+    l_run = (lpart[0] + lpart[1]) + (lpart[2] + lpart[3]);
   };
 
   const std::integral_constant<int, 0> tile0{};
