@@ -563,8 +563,13 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
       const int lim = kv_len - 1 - tk * kBlockN;
       const char* vt = vbytes + (int64_t)tv * C::kVTile;
       const char* ga[C::kKDma + C::kVDma];
+      if (lim >= kBlockN - 1) {
 #pragma unroll
-      for (int i = 0; i < C::kKDma; ++i) ga[i] = kt + (uint32_t)(min(kdma_row[i], lim) * krow_bytes + kdma_off[i]);
+        for (int i = 0; i < C::kKDma; ++i) ga[i] = kt + kdma_full[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < C::kKDma; ++i) ga[i] = kt + (uint32_t)(min(kdma_row[i], lim) * krow_bytes + kdma_off[i]);
+      }
 #pragma unroll
       for (int i = 0; i < C::kVDma; ++i) ga[C::kKDma + i] = vt + vdma_off[i];
       score_phase(k_read, v_read, s_cur, s_next, c_cur, mref, vr, pf, hv, [&](int g) {
