@@ -72,6 +72,8 @@ vdit_status_t validate_desc(const vdit_attn_desc_t& d) {
   const int64_t row = (int64_t)d.heads_total * d.head_dim * (d.layout == VDIT_LAYOUT_N3HD ? 3 : 1);
   const int64_t nmax = d.nq > d.nk ? d.nq : d.nk;
   if (row > (int64_t(1) << 40) || batch * nmax * row > (int64_t(1) << 60)) return VDIT_ERR_INVALID_ARG;
+  // the kernels address a 64-key tile's rows with 32-bit byte offsets (row * stride * 2)
+  if (int64_t(vdit::kBlockN) * row * 2 >= (int64_t(1) << 31)) return VDIT_ERR_UNSUPPORTED;
   if (d.use_rope) {
     if (d.nq != d.nk) return VDIT_ERR_INVALID_ARG;
     if (d.grid_t < 1 || d.grid_h < 1 || d.grid_w < 1) return VDIT_ERR_INVALID_ARG;

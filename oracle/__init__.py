@@ -35,7 +35,6 @@ from .attention import (  # noqa: F401
     rope_pair_bands,
     rope_index_table,
     rope_apply,
-    attention_weights,
     attention_rows,
     mha_reference,
 )

@@ -114,20 +114,6 @@ def rope_apply(u: np.ndarray, tokens, grid, dims, base: float) -> np.ndarray:
 # Attention.
 # ---------------------------------------------------------------------------
 
-def attention_weights(q: np.ndarray, k: np.ndarray, scale: float, key_len: int | None = None) -> np.ndarray:
-    """Softmax weights [R, L] of queries q [R, d] over keys k [Nk, d], keys j < L only.
-
-    s_j = scale * <q, k_j>; m = max_j s_j; w_j = exp(s_j - m) / sum_j exp(s_j - m).
-    """
-    L = k.shape[0] if key_len is None else int(key_len)
-    if not 1 <= L <= k.shape[0]:
-        raise ValueError("key length must be in [1, Nk]")
-    s = (q @ k[:L].T) * scale
-    m = s.max(axis=1, keepdims=True)
-    e = np.exp(s - m)
-    return e / e.sum(axis=1, keepdims=True)
-
-
 def attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
                    key_len: int | None = None, row_block: int = 256) -> np.ndarray:
     """Exact two-pass softmax attention for one head: q [R, d], k/v [Nk, d] -> [R, d]."""

@@ -111,10 +111,22 @@ ROPE = {"grid": (4, 32, 32), "dims": (44, 42, 42), "base": 10000.0}
     (dict(qk_int8=True, head_dim=64), UNSUPPORTED),
     (dict(qk_int8=True, rope=ROPE), UNSUPPORTED),
     (dict(qk_int8=True, nq=64, nk=262145), UNSUPPORTED),
+    # a 64-key tile's row offsets must fit 32-bit byte offsets: 64 * token stride * 2 < 2^31
+    (dict(nq=64, nk=64, heads_total=131072, head_count=1), UNSUPPORTED),
+    (dict(nq=64, nk=64, heads_total=43691, head_count=1, layout="N3HD"), UNSUPPORTED),
 ])
 def test_create_rejects_bad_descriptors(lib, kw, code):
     st, h = vd.create_raw(_desc(**kw))
     assert st == code and h == 0
+
+
+def test_largest_token_stride_is_accepted(lib):
+    for kw in (dict(heads_total=131071), dict(heads_total=43690, layout="N3HD")):
+        # validation passes; without a device, create then reports DEVICE
+        st, h = vd.create_raw(_desc(nq=64, nk=64, head_count=1, **kw))
+        assert st in (0, 5), kw
+        if h:
+            assert lib.vdit_attn_destroy(ctypes.c_void_p(h)) == 0
 
 
 def test_batch_zero_reads_as_one():

@@ -179,15 +179,6 @@ def test_attention_pins():
     assert attention_pins(oa.attention_rows) == []
 
 
-def test_attention_weights_sum_to_one():
-    rng = np.random.default_rng(3)
-    q = rng.standard_normal((9, 32)); k = rng.standard_normal((50, 32))
-    w = oracle.attention_weights(q, k, 0.3, 37)
-    assert w.shape == (9, 37)
-    assert np.allclose(w.sum(1), 1.0, rtol=0, atol=1e-12)
-    assert np.all(w > 0)
-
-
 def test_attention_rejects_empty_key_set():
     q = np.zeros((1, 4)); k = np.zeros((3, 4))
     with pytest.raises(ValueError):
