@@ -34,9 +34,14 @@
  * float32, taken relative to a fixed per-row reference (the maximum over the
  * first 64 keys; rows are recomputed with the exact maximum if a weight would
  * leave the float16 range); the weights are rounded to float16 and
- * v is converted once to float16 for the weighted sum (float32 accumulation);
- * the output is rounded to bfloat16 (nearest even). v values must lie within the
- * float16 range (|v| <= 65504).
+ * v is converted once to float16 for the weighted sum (float32 accumulation),
+ * after scaling each (entry, head) of v by the power of two 2^e that brings its
+ * largest |v| over the valid keys into [2^14, 2^15) (e limited to [-113, 64]);
+ * the output is multiplied by 2^-e, which undoes the scaling exactly. So every
+ * finite bfloat16 v works: none overflows, and values down to 2^-29 of the
+ * head's largest convert to float16 exactly (for a largest |v| of at least
+ * 2^-49; below that the scaling stops at 2^64). The output is rounded to
+ * bfloat16 (nearest even).
  * Batch. One call may carry B independent sequences of the same shape, e.g.
  * the positive and negative conditioning of classifier-free guidance (ComfyUI
  * issue "MultiGPU Work Units": diffusion models usually run two conditionings,
@@ -169,7 +174,10 @@ vdit_status_t vdit_attn_destroy(vdit_attn_t h);
  * Bytes of caller-provided device workspace that prepare/attend/fwd need for the
  * largest key length of this plan: v transposed to float16 per entry and head
  * ([B][head_count][ceil(nk/64)*64][d], 2 bytes) and, with use_rope, the rotated keys
- * (same shape, bfloat16). Host only.
+ * (same shape, bfloat16), then the qk_int8 regions (above), then the range of v:
+ * float [B][head_count][64] partial maxima of |v| and int32 [B][head_count] scaling
+ * exponents e. Each region after the first starts at the next multiple of 256
+ * bytes. Host only.
  */
 vdit_status_t vdit_attn_workspace_bytes(vdit_attn_t h, size_t* bytes);
 
@@ -190,9 +198,9 @@ vdit_status_t vdit_attn_fwd(vdit_attn_t h, const void* q, const void* k, const v
                             void* hip_stream);
 
 /*
- * First stage of fwd: writes v (heads of the share, keys < key_len) transposed
- * and converted to float16 into the workspace, zero-filled up to the next
- * multiple of 64 keys; with use_rope also the rotated keys (bfloat16); with
+ * First stage of fwd: finds the range of v (heads of the share, keys < key_len)
+ * and writes v, scaled by 2^e, transposed and converted to float16 into the
+ * workspace, zero-filled up to the next multiple of 64 keys; with use_rope also the rotated keys (bfloat16); with
  * qk_int8 the int8 codes and scales of q and of the valid keys. Arguments
  * as for fwd (q is read only for the N3HD layout, where it is the packed tensor).
  */

@@ -21,6 +21,8 @@ struct vdit_attn {
   // int8 q.k: codes and scales per (entry, head)
   int64_t nq_pad;      // queries rounded up to the q quantization block
   size_t ws_qc_off, ws_kc_off, ws_qs_off, ws_ks_off;
+  // range of v per (entry, head): partial maxima and the exponent of its scaling
+  size_t ws_vpart_off, ws_vexp_off;
   size_t ws_total;
   float2* rope_tab;    // device (cos, sin) table, or nullptr
   vdit::RopeGeom geom;
@@ -211,6 +213,8 @@ vdit_status_t do_prepare(const vdit_attn& h, const Inputs& in, const KeyLens& kl
   a.hc = d.head_count;
   a.batch = d.batch;
   a.rope = h.geom;
+  a.vpart = reinterpret_cast<float*>(static_cast<char*>(ws) + h.ws_vpart_off);
+  a.vexp = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + h.ws_vexp_off);
   for (int32_t b = 0; b < vdit::kMaxBatch; ++b) a.kv_len[b] = kl.len[b];
   if (vdit::launch_prepare(a, d.head_dim, d.use_rope != 0, s) != hipSuccess) return VDIT_ERR_DEVICE;
   if (d.qk_int8) {
@@ -270,6 +274,7 @@ vdit_status_t do_attend(const vdit_attn& h, const Inputs& in, const KeyLens& kl,
   a.batch = d.batch;
   a.c = h.c;
   a.rope = h.geom;
+  a.vexp = reinterpret_cast<const int32_t*>(static_cast<const char*>(ws) + h.ws_vexp_off);
   if (d.qk_int8) {
     const char* w = static_cast<const char*>(ws);
     a.c = 1.4426950408889634f;  // log2(e): the softmax scale is inside the q codes
@@ -350,6 +355,12 @@ vdit_status_t vdit_attn_create(const vdit_attn_desc_t* desc, vdit_attn_t* out) {
     h.ws_qs_off = align_up(h.ws_kc_off + slices * h.nk_pad * d.head_dim, 256);
     h.ws_ks_off = align_up(h.ws_qs_off + slices * (h.nq_pad / vdit::kQuantQ) * sizeof(float), 256);
     h.ws_total = h.ws_ks_off + slices * (h.nk_pad / vdit::kQuantK) * sizeof(float);
+  }
+  {
+    const size_t slices = (size_t)d.head_count * d.batch;
+    h.ws_vpart_off = align_up(h.ws_total, 256);
+    h.ws_vexp_off = align_up(h.ws_vpart_off + slices * vdit::kVParts * sizeof(float), 256);
+    h.ws_total = h.ws_vexp_off + slices * sizeof(int32_t);
   }
   h.rope_tab = nullptr;
   h.geom = vdit::RopeGeom{};
@@ -607,6 +618,7 @@ vdit_status_t do_vsa_attend(const vdit_attn& h, const Inputs& in, int32_t keep, 
   a.c = h.c;
   a.tiles = tiles;
   a.keep = keep;
+  a.vexp = reinterpret_cast<const int32_t*>(static_cast<const char*>(ws) + h.ws_vexp_off);
   for (int32_t b = 0; b < vdit::kMaxBatch; ++b) a.kv_len[b] = kl.len[b];
   if (vdit::launch_attn_sparse(a, d.head_dim, s) != hipSuccess) return VDIT_ERR_DEVICE;
   return VDIT_OK;

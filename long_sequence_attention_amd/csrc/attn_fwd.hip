@@ -740,7 +740,8 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   }
   {
     const float lt = KS == 2 ? l_run[0] : l_run[0] + __shfl_xor(l_run[0], 32);
-    const float inv = 1.0f / lt;
+    // 1 / row sum, times 2^-e to undo the power-of-two scaling of v (exact)
+    const float inv = __builtin_amdgcn_ldexpf(1.0f / lt, -a.vexp[bh]);
     const int swz = 2 * (l32 & (kGran - 1));
 #pragma unroll
     for (int db = 0; db < C::kDB; ++db)

@@ -396,7 +396,8 @@ __global__ void __launch_bounds__(kResThreads) attn_resident_kernel(AttnArgs a, 
     constexpr int kGran = D / 8;
     constexpr int kRowsPerStore = kWave / kGran;
     static_assert((kRowBytes & (kRowBytes - 1)) == 0 && kResEpiBytes % kRowBytes == 0, "row alignment");
-    const float inv = 1.0f / (l_run + __shfl_xor(l_run, 32));
+    // 1 / row sum, times 2^-e to undo the power-of-two scaling of v (exact)
+    const float inv = __builtin_amdgcn_ldexpf(1.0f / (l_run + __shfl_xor(l_run, 32)), -a.vexp[bh]);
     const uint32_t stg = lds_addr(e_lds) + wave_u * kResEpiBytes;
     const int q0 = qt * kResQ + wave * 32;
     __bf16* obase = a.out + bat * a.out_batch + (int64_t)head * D;

@@ -108,6 +108,24 @@ constexpr int kSmallKeys = 1024;
 constexpr int kVsaMaxTiles = 8192;  // key tiles one selection can rank (32 keys per thread of the select kernel)
 constexpr int kVsaMaxKeep = 4096;   // kept tiles per query tile (the attention kernel's LDS list)
 
+// v is converted to float16 for the weighted sum after scaling by a power of two
+// 2^e per (entry, head), chosen from max |v| over the valid keys so that the
+// largest value lands in [2^14, 2^15): every bfloat16 value within 2^29 of the
+// maximum is then a normal float16 and converts exactly, and nothing overflows.
+// The epilogues multiply by 2^-e, which undoes the scaling exactly (a power of
+// two commutes with rounding). max |v| is reduced in two steps: kVParts partial
+// maxima per (entry, head), then each prepare workgroup combines them.
+constexpr int kVParts = 64;
+constexpr int kVExpMin = -113;  // bfloat16's largest finite value still lands below 2^15
+constexpr int kVExpMax = 64;    // keeps 2^-e * (1 / row sum) a normal float in the epilogue
+
+// Exponent e of the scaling for a maximum |v| of `amax` (0, inf or NaN: e = 0).
+__device__ __forceinline__ int v_scale_exp(float amax) {
+  if (!(amax > 0.0f) || amax > 3.4028235e38f) return 0;
+  const int e = 15 - __builtin_amdgcn_frexp_expf(amax);  // amax = f * 2^ex, 0.5 <= f < 1
+  return e < kVExpMin ? kVExpMin : (e > kVExpMax ? kVExpMax : e);
+}
+
 // Element offsets of batch entry b are b * (the *_batch stride) on top of those below.
 struct AttnArgs {
   const __bf16* q;       // q of head `head_begin`, token 0, entry 0
@@ -143,6 +161,7 @@ struct AttnArgs {
   // [bh][n_qtiles][keep], ascending
   const int32_t* tiles;
   int32_t keep;
+  const int32_t* vexp;   // [bh]: v was scaled by 2^vexp before the float16 conversion
   int32_t kv_len[kMaxBatch];  // valid keys of each entry
 };
 
@@ -180,6 +199,8 @@ struct PrepArgs {
   int32_t hc;
   int32_t batch;
   RopeGeom rope;
+  float* vpart;          // [bh][kVParts] partial maxima of |v|
+  int32_t* vexp;         // [bh] exponent of the v scaling (written by key tile 0)
   int32_t kv_len[kMaxBatch];
 };
 

@@ -1,5 +1,7 @@
 // Bandwidth-bound kernels around the attention kernel:
-//   * prepare: v of the head share -> float16 V^T tiles in the workspace (keys
+//   * v range: partial maxima of |v| over the valid keys of each (entry, head);
+//   * prepare: v of the head share, scaled by the power of two 2^e that brings its
+//     maximum into [2^14, 2^15), -> float16 V^T tiles in the workspace (keys
 //     permuted inside groups of 16 to match the weight layout of the attention
 //     kernel, zero past the valid keys), and with RoPE the rotated keys;
 //   * quantize (int8 q.k): symmetric int8 codes and float32 scales of q (128
@@ -19,6 +21,44 @@ __device__ __forceinline__ int vt_position(int k) {
   return (k & ~15) | (k & 3) | ((k >> 1) & 4) | ((k << 1) & 8);
 }
 
+// Partial maximum of |v| over part blockIdx.x of the valid keys of (entry, head)
+// blockIdx.y; each part is a contiguous run of keys (possibly empty: then 0).
+template <int D>
+__global__ void __launch_bounds__(256) vrange_kernel(PrepArgs a) {
+  constexpr int kChunks = D / 8;
+  __shared__ float red[4];
+  const int part = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int bat = bh / a.hc;
+  const int head = bh - bat * a.hc;
+  const int kv_len = a.kv_len[bat];
+  const int per = (kv_len + kVParts - 1) / kVParts;
+  const int k0 = part * per;
+  const int k1 = min(kv_len, k0 + per);
+  const __bf16* vsrc = a.v + bat * a.kv_batch + (int64_t)head * a.kv_head;
+  float m = 0.0f;
+  const int total = max(k1 - k0, 0) * kChunks;
+  // four independent 16-byte loads per thread in flight
+  for (int c0 = threadIdx.x; c0 < total; c0 += 4 * 256) {
+    bf16x8 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = c0 + u * 256;
+      v[u] = c < total ? *reinterpret_cast<const bf16x8*>(vsrc + (int64_t)(k0 + c / kChunks) * a.kv_row + (c % kChunks) * 8)
+                       : bf16x8{};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf((float)v[u][e]));
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) a.vpart[(int64_t)bh * kVParts + part] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
 template <int D, bool ROPE>
 __global__ void __launch_bounds__(256) prepare_kernel(PrepArgs a) {
   constexpr int kChunks = D / 8;
@@ -35,6 +75,13 @@ __global__ void __launch_bounds__(256) prepare_kernel(PrepArgs a) {
   // tiles past this entry's keys are never read by the attention kernel
   if (tile * kBlockN >= kv_len) return;
   const __bf16* vsrc = a.v + bat * a.kv_batch + (int64_t)head * a.kv_head;
+  // the scaling of this (entry, head): every wave combines the partial maxima
+  static_assert(kVParts == kWave, "one partial maximum per lane");
+  float amax = a.vpart[(int64_t)bh * kVParts + (tid & 63)];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  const int vsh = v_scale_exp(amax);
+  if (tile == 0 && tid == 0) a.vexp[bh] = vsh;
 
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) {
@@ -46,7 +93,7 @@ __global__ void __launch_bounds__(256) prepare_kernel(PrepArgs a) {
     if (key < kv_len) v = *reinterpret_cast<const bf16x8*>(vsrc + (int64_t)key * a.kv_row + ch * 8);
     const int pos = vt_position(kl);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) tr[(ch * 8 + e) * kPad + pos] = (_Float16)(float)v[e];
+    for (int e = 0; e < 8; ++e) tr[(ch * 8 + e) * kPad + pos] = (_Float16)__builtin_amdgcn_ldexpf((float)v[e], vsh);
   }
   __syncthreads();
   _Float16* dst = a.vt + (int64_t)bh * a.vt_head + (int64_t)tile * (D * kBlockN);
@@ -183,6 +230,7 @@ __global__ void __launch_bounds__(256) rope_probe_kernel(RopeGeom g, int32_t nq,
 
 template <int D, bool ROPE>
 hipError_t launch_prepare_t(const PrepArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((vrange_kernel<D>), dim3(kVParts, a.hc * a.batch), dim3(256), 0, s, a);
   hipLaunchKernelGGL((prepare_kernel<D, ROPE>), dim3(a.n_ktiles, a.hc * a.batch), dim3(256), 0, s, a);
   return hipGetLastError();
 }
@@ -190,7 +238,8 @@ hipError_t launch_prepare_t(const PrepArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_prepare(const PrepArgs& a, int head_dim, bool rope_k, hipStream_t s) {
-  if (a.n_ktiles <= 0 || a.hc <= 0 || a.batch <= 0 || a.batch > kMaxBatch || (int64_t)a.hc * a.batch > 65535)
+  if (a.n_ktiles <= 0 || a.hc <= 0 || a.batch <= 0 || a.batch > kMaxBatch || (int64_t)a.hc * a.batch > 65535 ||
+      !a.vpart || !a.vexp)
     return hipErrorInvalidValue;
   if (head_dim == 128) return rope_k ? launch_prepare_t<128, true>(a, s) : launch_prepare_t<128, false>(a, s);
   if (head_dim == 64) return rope_k ? launch_prepare_t<64, true>(a, s) : launch_prepare_t<64, false>(a, s);

@@ -13,7 +13,7 @@ import torch
 import oracle
 from oracle import int8_qk
 import synthetic_inputs as si
-from test_gpu_parity import as_f64, check, note, up
+from test_gpu_parity import as_f64, check, note, up, workspace_layout
 
 pytestmark = pytest.mark.gpu
 
@@ -32,22 +32,9 @@ def vdm():
     return vd
 
 
-def align(x, a=256):
-    return (x + a - 1) // a * a
-
-
 def ws_regions(B, hc, nq, nk, d=128):
     """Byte offsets of the int8 regions, as the header lays the workspace out."""
-    nk_pad = (nk + 63) // 64 * 64
-    nq_pad = (nq + 127) // 128 * 128
-    s = B * hc
-    vt = s * nk_pad * d * 2
-    qc = align(vt)
-    kc = align(qc + s * nq_pad * d)
-    qs = align(kc + s * nk_pad * d)
-    ks = align(qs + s * (nq_pad // 128) * 4)
-    end = ks + s * (nk_pad // 64) * 4
-    return dict(nq_pad=nq_pad, nk_pad=nk_pad, qc=qc, kc=kc, qs=qs, ks=ks, end=end)
+    return workspace_layout(B, hc, nq, nk, d, int8=True)
 
 
 def test_codes_and_scales_are_bit_exact(dev):
@@ -147,7 +134,22 @@ def test_ulysses_share_n75600_sampled_rows(dev):
     out = vd.Attention(n, n, 40, 128, head_begin=0, head_count=10, qk_int8=True).forward(up(q, dev), up(k, dev),
                                                                                        up(v, dev))
     torch.cuda.synchronize()
-    rows = si.sample_rows(n, 1024, 1003, si.tile_edge_rows(n))
+    rows = si.sample_rows(n, 4096, 1003, si.tile_edge_rows(n))
     got = as_f64(out[torch.from_numpy(rows).to(dev)])
     ref = oracle.mha_reference_qk_int8(q, k, v, head_begin=0, head_count=10, rows=rows)
     check(got, ref, f"int8 N={n} ({len(rows)} rows x 10 heads)")
+
+
+def test_scores_growing_past_first_tile_max_four_stage(dev):
+    # more than 1024 keys and 256 workgroups of 256 queries: the eight-wave,
+    # four-stage int8 kernel; the last keys overflow the first tile's reference,
+    # so its exact-maximum retry runs
+    from test_gpu_parity import growing_score_inputs
+    vd = vdm()
+    nq = nk = 4096
+    ht = 16
+    note(f"int8 growing scores, four-stage kernel: nq=nk={nq} heads={ht}")
+    q, k, v = growing_score_inputs(nq, nk, ht, 128, 9500)
+    out = vd.Attention(nq, nk, ht, 128, qk_int8=True).forward(up(q, dev), up(k, dev), up(v, dev))
+    torch.cuda.synchronize()
+    check(as_f64(out), oracle.mha_reference_qk_int8(q, k, v), "int8 growing scores 4-stage")
