@@ -36,12 +36,11 @@
  * leave the float16 range); the weights are rounded to float16 and
  * v is converted once to float16 for the weighted sum (float32 accumulation),
  * after scaling each (entry, head) of v by the power of two 2^e that brings its
- * largest |v| over the valid keys into [2^14, 2^15) (e limited to [-113, 64]);
- * the output is multiplied by 2^-e, which undoes the scaling exactly. So every
+ * largest |v| over the valid keys into [2^14, 2^15) (e in [-113, 160]); the
+ * output is multiplied by 2^-e, which undoes the scaling exactly. So every
  * finite bfloat16 v works: none overflows, and values down to 2^-29 of the
- * head's largest convert to float16 exactly (for a largest |v| of at least
- * 2^-49; below that the scaling stops at 2^64). The output is rounded to
- * bfloat16 (nearest even).
+ * head's largest convert to float16 exactly. The output is rounded to bfloat16
+ * (nearest even).
  * Batch. One call may carry B independent sequences of the same shape, e.g.
  * the positive and negative conditioning of classifier-free guidance (ComfyUI
  * issue "MultiGPU Work Units": diffusion models usually run two conditionings,

@@ -740,8 +740,19 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   }
   {
     const float lt = KS == 2 ? l_run[0] : l_run[0] + __shfl_xor(l_run[0], 32);
-    // 1 / row sum, times 2^-e to undo the power-of-two scaling of v (exact)
-    const float inv = __builtin_amdgcn_ldexpf(1.0f / lt, -a.vexp[bh]);
+    // 1 / row sum and the power-of-two unscaling of v (exact)
+    const VUnscale us = v_unscale(lt, a.vexp[bh]);
+    if (us.rest != 0) {
+#pragma unroll
+      for (int db = 0; db < C::kDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[0][db][r] = __builtin_amdgcn_ldexpf(o[0][db][r] * us.inv, us.rest);
+    } else {
+#pragma unroll
+      for (int db = 0; db < C::kDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[0][db][r] *= us.inv;
+    }
     const int swz = 2 * (l32 & (kGran - 1));
 #pragma unroll
     for (int db = 0; db < C::kDB; ++db)
@@ -749,7 +760,7 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
       for (int g = 0; g < 4; ++g) {
         bf16x4 w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[0][db][4 * g + e] * inv);
+        for (int e = 0; e < 4; ++e) w[e] = (__bf16)o[0][db][4 * g + e];
         const int c = db * 8 + 2 * g + hl;     // 8-byte piece of the row
         *reinterpret_cast<bf16x4*>(stg + l32 * kRowBytes + ((c ^ swz) << 3)) = w;
       }

@@ -396,8 +396,19 @@ __global__ void __launch_bounds__(kResThreads) attn_resident_kernel(AttnArgs a, 
     constexpr int kGran = D / 8;
     constexpr int kRowsPerStore = kWave / kGran;
     static_assert((kRowBytes & (kRowBytes - 1)) == 0 && kResEpiBytes % kRowBytes == 0, "row alignment");
-    // 1 / row sum, times 2^-e to undo the power-of-two scaling of v (exact)
-    const float inv = __builtin_amdgcn_ldexpf(1.0f / (l_run + __shfl_xor(l_run, 32)), -a.vexp[bh]);
+    // 1 / row sum and the power-of-two unscaling of v (exact)
+    const VUnscale us = v_unscale(l_run + __shfl_xor(l_run, 32), a.vexp[bh]);
+    if (us.rest != 0) {
+#pragma unroll
+      for (int db = 0; db < C::kDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] = __builtin_amdgcn_ldexpf(o[db][r] * us.inv, us.rest);
+    } else {
+#pragma unroll
+      for (int db = 0; db < C::kDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= us.inv;
+    }
     const uint32_t stg = lds_addr(e_lds) + wave_u * kResEpiBytes;
     const int q0 = qt * kResQ + wave * 32;
     __bf16* obase = a.out + bat * a.out_batch + (int64_t)head * D;
@@ -415,7 +426,7 @@ __global__ void __launch_bounds__(kResThreads) attn_resident_kernel(AttnArgs a, 
           for (int g = 0; g < 4; ++g) {
             bf16x4 w;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[db][4 * g + e] * inv);
+            for (int e = 0; e < 4; ++e) w[e] = (__bf16)o[db][4 * g + e];
             const int pc = db * 8 + 2 * g;  // 8-byte piece of the row (plus hl)
             *(__attribute__((address_space(3))) bf16x4*)(uintptr_t)(wb ^ (uint32_t)(pc << 3)) = w;
           }

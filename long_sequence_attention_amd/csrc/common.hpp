@@ -117,13 +117,28 @@ constexpr int kVsaMaxKeep = 4096;   // kept tiles per query tile (the attention 
 // maxima per (entry, head), then each prepare workgroup combines them.
 constexpr int kVParts = 64;
 constexpr int kVExpMin = -113;  // bfloat16's largest finite value still lands below 2^15
-constexpr int kVExpMax = 64;    // keeps 2^-e * (1 / row sum) a normal float in the epilogue
+constexpr int kVExpMax = 160;   // below bfloat16's smallest subnormal
+// The epilogue folds min(e, kVExpFold) into 1 / row sum (which stays a normal float:
+// the row sum is at most 2^47) and applies the rest of e to each output value.
+constexpr int kVExpFold = 64;
 
 // Exponent e of the scaling for a maximum |v| of `amax` (0, inf or NaN: e = 0).
 __device__ __forceinline__ int v_scale_exp(float amax) {
   if (!(amax > 0.0f) || amax > 3.4028235e38f) return 0;
   const int e = 15 - __builtin_amdgcn_frexp_expf(amax);  // amax = f * 2^ex, 0.5 <= f < 1
   return e < kVExpMin ? kVExpMin : (e > kVExpMax ? kVExpMax : e);
+}
+
+// Epilogue factors undoing the scaling 2^e of v: out = ldexp(o * inv, rest), with
+// inv = 2^-min(e, kVExpFold) / row sum and rest = min(e, kVExpFold) - e (0 unless v
+// was below about 2^-49, so the per-value ldexp is skipped).
+struct VUnscale {
+  float inv;
+  int rest;
+};
+__device__ __forceinline__ VUnscale v_unscale(float row_sum, int e) {
+  const int fold = e < kVExpFold ? e : kVExpFold;
+  return VUnscale{__builtin_amdgcn_ldexpf(1.0f / row_sum, -fold), fold - e};
 }
 
 // Element offsets of batch entry b are b * (the *_batch stride) on top of those below.

@@ -220,22 +220,34 @@ def test_packed_rope_n131072(packed_rope_run):
 
 @pytest.mark.timeout(600)
 def test_packed_rope_rotated_keys_match_float64_rope(packed_rope_run):
-    # the pre-pass rotates k in float32 with float32 cos/sin; the float64 rotation
-    # rounded once to bfloat16 must agree on >= 99.9% of the elements, the rest
-    # within one bfloat16 ulp (a float32 rounding error crossing a bfloat16
-    # rounding boundary)
+    # The pre-pass rotates k in float32 with float32 cos/sin; the float64 rotation
+    # rounded once to bfloat16 must agree bit for bit on >= 99.9% of the elements.
+    # The rest must be within one bfloat16 ulp, or, where the rotation of a pair
+    # (a, b) cancels to a value much smaller than the pair, within the float32
+    # error of the rotation itself (a few 2^-24 (|a| + |b|); 2^-21 allowed): such
+    # an output has bfloat16 ulps far below float32's resolution of the pair.
     qkv, _, _, kr = packed_rope_run
     n = qkv.shape[0]
     tokens = np.arange(n)
     for h in ROPE_K_HEADS:
         k = oracle.bf16_bits_to_f64(qkv[:, 1, h, :])
-        want = f64_to_bf16_bits(oracle.rope_apply(k, tokens, ROPE5["grid"], ROPE5["dims"], ROPE5["base"]))
+        exact = oracle.rope_apply(k, tokens, ROPE5["grid"], ROPE5["dims"], ROPE5["base"])
+        want = f64_to_bf16_bits(exact)
         gotb = kr[h][:n]
         diff = np.abs(bf16_order(gotb) - bf16_order(want))
-        exact = float((diff == 0).mean())
-        note(f"rotated k head {h}: {exact * 100:.4f}% exact, max ulp difference {int(diff.max())}")
-        assert exact >= 0.999, h
-        assert int(diff.max()) <= 1, h
+        share = float((diff == 0).mean())
+        pair = np.abs(k[:, 0::2]) + np.abs(k[:, 1::2])
+        pair = np.repeat(pair, 2, axis=1)
+        got = oracle.bf16_bits_to_f64(gotb)
+        mag = np.maximum(np.abs(got), np.abs(exact))
+        ulp = np.ldexp(1.0, np.frexp(mag)[1] - 8)
+        far = diff > 1
+        note(f"rotated k head {h}: {share * 100:.4f}% exact, {int(far.sum())} elements beyond one ulp "
+             f"(max {int(diff.max())} ulp, all at |k'| / (|a| + |b|) <= "
+             f"{float((mag[far] / pair[far]).max()) if far.any() else 0.0:.2e})")
+        assert share >= 0.999, h
+        assert np.all(np.abs(got - exact) <= ulp + 2.0 ** -21 * pair), h
+        assert float(far.mean()) <= 1e-4, h
 
 
 # ---------------------------------------------------------------------------
@@ -535,8 +547,8 @@ def test_value_scale_n4096_h10(dev, sigma_v):
 
 def test_value_scales_differ_per_head(dev):
     # one call, heads of very different magnitude: each head gets its own scaling
-    scales = [3e-7, 1.0, 7e5, 2e-30, 5e35, 1e-3]
-    q, k, v = nhd_inputs(1500, 1500, 6, 128, 9600)
+    scales = [3e-7, 1.0, 7e5, 2e-30, 5e35, 1e-3, 1e-33, 1e-20]
+    q, k, v = nhd_inputs(1500, 1500, 8, 128, 9600)
     v = scaled_values(v, scales)
     out = as_f64(run_nhd(dev, q, k, v))
     ref = oracle.mha_reference(q, k, v)
