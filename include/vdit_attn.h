@@ -218,6 +218,22 @@ vdit_status_t vdit_attn_attend(vdit_attn_t h, const void* q, const void* k, cons
                                void* hip_stream);
 
 /*
+ * vdit_attn_fwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). The workspace regions (vdit_attn_workspace_bytes)
+ * live instead in a fixed 256 MiB device array of the library, one copy per GPU,
+ * reserved while the library is loaded and looked up on the first call on each
+ * device. The call allocates nothing. UNSUPPORTED if the plan needs more than
+ * 256 MiB of workspace (one head share of 10 heads at 75600 tokens needs
+ * 194 MB and fits). Every call on a GPU uses that GPU's one array: calls that overlap in
+ * time on one GPU (other streams, other threads) race and give undefined
+ * results; calls ordered on one stream are safe. Nothing from an earlier call is
+ * read. Other arguments and errors as for vdit_attn_fwd.
+ */
+vdit_status_t vdit_attn_fwd_noalloc(vdit_attn_t h, const void* q, const void* k, const void* v,
+                                    int32_t key_len, void* out, void* hip_stream);
+
+/*
  * fwd, prepare and attend with one key length per batch entry, for batches whose
  * sequences mask different numbers of keys (e.g. positive and negative prompts of
  * different text lengths under classifier-free guidance). key_lens: host array of

@@ -41,6 +41,7 @@ SIGNATURES = {
     "vdit_attn_fwd": (_ST, [_P, _P, _P, _P, _I, _P, _P, _S, _P]),
     "vdit_attn_prepare": (_ST, [_P, _P, _P, _P, _I, _P, _S, _P]),
     "vdit_attn_attend": (_ST, [_P, _P, _P, _P, _I, _P, _P, _S, _P]),
+    "vdit_attn_fwd_noalloc": (_ST, [_P, _P, _P, _P, _I, _P, _P]),
     "vdit_attn_fwd_lens": (_ST, [_P, _P, _P, _P, ctypes.POINTER(_I), _P, _P, _S, _P]),
     "vdit_attn_prepare_lens": (_ST, [_P, _P, _P, _P, ctypes.POINTER(_I), _P, _S, _P]),
     "vdit_attn_attend_lens": (_ST, [_P, _P, _P, _P, ctypes.POINTER(_I), _P, _P, _S, _P]),

@@ -171,6 +171,17 @@ class Attention:
 
     __call__ = forward
 
+    def forward_noalloc(self, q, k=None, v=None, *, key_len: int = 0, out=None, stream=None):
+        """forward without a workspace: the library's fixed per-GPU array holds it
+        (vdit_attn_fwd_noalloc; calls overlapping in time on one GPU race)."""
+        self._check_inputs(q, k, v)
+        if out is None:
+            out = torch.empty(self.out_shape, dtype=torch.bfloat16, device=q.device)
+        _need(out, self.out_shape, torch.bfloat16, "out")
+        _check(self._lib.vdit_attn_fwd_noalloc(self._h, _ptr(q), _ptr(k), _ptr(v), int(key_len), _ptr(out),
+                                               _stream_ptr(q, stream)), "vdit_attn_fwd_noalloc")
+        return out
+
     def prepare(self, q, k=None, v=None, *, key_len: int = 0, key_lens=None, workspace=None, stream=None):
         self._check_inputs(q, k, v)
         ws = self._ws(workspace, q.device)

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libvdit_attn.so")
-SOURCES = ["attn_fwd.hip", "attn_resident.hip", "prepass.hip", "vsa.hip", "api.hip"]
+SOURCES = ["attn_fwd.hip", "attn_resident.hip", "prepass.hip", "vsa.hip", "api.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

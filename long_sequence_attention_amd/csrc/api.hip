@@ -8,6 +8,7 @@
 #include <vector>
 
 #include "common.hpp"
+#include "entry.hpp"
 #include "vdit_attn.h"
 
 struct vdit_attn {
@@ -435,6 +436,23 @@ vdit_status_t run(vdit_attn_t h, const void* q, const void* k, const void* v, bo
 }
 
 }  // namespace
+
+// ---- internal entry points for the fixed-workspace variant (noalloc.hip)
+namespace vdit {
+
+vdit_status_t plan_workspace(vdit_attn_t h, size_t* bytes, int* device) {
+  if (!is_live(h) || !bytes || !device) return VDIT_ERR_INVALID_ARG;
+  *bytes = h->ws_total;
+  *device = h->device;
+  return VDIT_OK;
+}
+
+vdit_status_t fwd_into_workspace(vdit_attn_t h, const void* q, const void* k, const void* v, int32_t key_len,
+                                 void* out, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return run(h, q, k, v, false, key_len, nullptr, out, workspace, workspace_bytes, hip_stream, Stage::kBoth);
+}
+
+}  // namespace vdit
 
 extern "C" {
 

@@ -34,7 +34,7 @@ def header_functions():
 
 def test_library_exports_every_declared_symbol(lib):
     names = header_functions()
-    assert len(names) == 19
+    assert len(names) == 20
     assert sorted(names) == sorted(_lib.SIGNATURES)
     for n in names:
         assert hasattr(lib, n), n
@@ -150,6 +150,7 @@ def test_handle_checks_without_device(lib):
     assert lib.vdit_attn_fwd(bogus, None, None, None, 1, None, None, 0, None) == INVALID
     assert lib.vdit_attn_prepare(bogus, None, None, None, 1, None, 0, None) == INVALID
     assert lib.vdit_attn_attend(bogus, None, None, None, 1, None, None, 0, None) == INVALID
+    assert lib.vdit_attn_fwd_noalloc(bogus, None, None, None, 1, None, None) == INVALID
     lens = (ctypes.c_int32 * 2)(5, 7)
     assert lib.vdit_attn_fwd_lens(bogus, None, None, None, lens, None, None, 0, None) == INVALID
     assert lib.vdit_attn_prepare_lens(bogus, None, None, None, lens, None, 0, None) == INVALID
