@@ -32,8 +32,8 @@
  *
  * Numerics: q.k products in bfloat16 with float32 accumulation; softmax in
  * float32, taken relative to a fixed per-row reference (the maximum over the
- * first 64 keys; rows are recomputed with the exact maximum if a weight would
- * leave the float16 range); the weights are rounded to float16 and
+ * first 64 keys; rows where a weight would leave the float16 range are listed and
+ * recomputed with the exact maximum by a second launch); the weights are rounded to float16 and
  * v is converted once to float16 for the weighted sum (float32 accumulation),
  * after scaling each (entry, head) of v by the power of two 2^e that brings its
  * largest |v| over the valid keys into [2^14, 2^15) (e in [-113, 160]); the
@@ -175,8 +175,10 @@ vdit_status_t vdit_attn_destroy(vdit_attn_t h);
  * ([B][head_count][ceil(nk/64)*64][d], 2 bytes) and, with use_rope, the rotated keys
  * (same shape, bfloat16), then the qk_int8 regions (above), then the range of v:
  * float [B][head_count][64] partial maxima of |v| and int32 [B][head_count] scaling
- * exponents e. Each region after the first starts at the next multiple of 256
- * bytes. Host only.
+ * exponents e; then the retry list of the rows whose float16 weights overflowed:
+ * int32 [B][head_count][2] counters (cleared by prepare, zero again after attend)
+ * and int32 [B][head_count][nq] rows. Each region after the first starts at the
+ * next multiple of 256 bytes. Host only.
  */
 vdit_status_t vdit_attn_workspace_bytes(vdit_attn_t h, size_t* bytes);
 

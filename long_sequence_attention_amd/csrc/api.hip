@@ -24,6 +24,8 @@ struct vdit_attn {
   size_t ws_qc_off, ws_kc_off, ws_qs_off, ws_ks_off;
   // range of v per (entry, head): partial maxima and the exponent of its scaling
   size_t ws_vpart_off, ws_vexp_off;
+  // rows whose float16 weights overflowed: counters and row lists per (entry, head)
+  size_t ws_rcnt_off, ws_rrows_off;
   size_t ws_total;
   float2* rope_tab;    // device (cos, sin) table, or nullptr
   vdit::RopeGeom geom;
@@ -216,6 +218,7 @@ vdit_status_t do_prepare(const vdit_attn& h, const Inputs& in, const KeyLens& kl
   a.rope = h.geom;
   a.vpart = reinterpret_cast<float*>(static_cast<char*>(ws) + h.ws_vpart_off);
   a.vexp = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + h.ws_vexp_off);
+  a.retry_cnt = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + h.ws_rcnt_off);
   for (int32_t b = 0; b < vdit::kMaxBatch; ++b) a.kv_len[b] = kl.len[b];
   if (vdit::launch_prepare(a, d.head_dim, d.use_rope != 0, s) != hipSuccess) return VDIT_ERR_DEVICE;
   if (d.qk_int8) {
@@ -276,6 +279,8 @@ vdit_status_t do_attend(const vdit_attn& h, const Inputs& in, const KeyLens& kl,
   a.c = h.c;
   a.rope = h.geom;
   a.vexp = reinterpret_cast<const int32_t*>(static_cast<const char*>(ws) + h.ws_vexp_off);
+  a.retry_cnt = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + h.ws_rcnt_off);
+  a.retry_rows = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + h.ws_rrows_off);
   if (d.qk_int8) {
     const char* w = static_cast<const char*>(ws);
     a.c = 1.4426950408889634f;  // log2(e): the softmax scale is inside the q codes
@@ -361,7 +366,9 @@ vdit_status_t vdit_attn_create(const vdit_attn_desc_t* desc, vdit_attn_t* out) {
     const size_t slices = (size_t)d.head_count * d.batch;
     h.ws_vpart_off = align_up(h.ws_total, 256);
     h.ws_vexp_off = align_up(h.ws_vpart_off + slices * vdit::kVParts * sizeof(float), 256);
-    h.ws_total = h.ws_vexp_off + slices * sizeof(int32_t);
+    h.ws_rcnt_off = align_up(h.ws_vexp_off + slices * sizeof(int32_t), 256);
+    h.ws_rrows_off = align_up(h.ws_rcnt_off + slices * 2 * sizeof(int32_t), 256);
+    h.ws_total = h.ws_rrows_off + slices * (size_t)d.nq * sizeof(int32_t);
   }
   h.rope_tab = nullptr;
   h.geom = vdit::RopeGeom{};

@@ -34,9 +34,13 @@
 // Softmax: the weights use a fixed reference, the row maximum of the first key
 // tile, in the log2 domain (c = scale * log2 e): p = 2^(s*c - m). O is never
 // rescaled. If some later score exceeds the reference by more than the float16
-// range allows, a weight becomes inf and the row sum non-finite; the workgroup
-// then recomputes its rows with the exact row maximum. The row sum is taken from
-// the rounded float16 weights (v_dot2), the same values the product uses.
+// range allows, a weight becomes inf and the row sum non-finite; such rows are
+// appended to a retry list of their (entry, head), and a second launch of the
+// same kernel (RETRY) recomputes only the listed rows, 256 per workgroup, with
+// the exact row maximum (a q.k-only pass for the maximum, then the normal pass,
+// where every weight is at most 1). In the block-sparse mode the workgroup
+// recomputes its own rows instead. The row sum is taken from the rounded float16
+// weights (v_dot2), the same values the product uses.
 #include "common.hpp"
 #include "lds.hpp"
 
@@ -72,7 +76,9 @@ struct FwdCfg {
 // quantize pre-pass with the softmax scale folded into q. The integer scores come
 // out of the products already readable as floats (offset by a constant, see
 // qk_mfma); each tile's weights use c = q scale * k scale * log2 e per lane.
-template <int D, int QB, int WAVES, int NST, bool ROPE, bool QK8, bool SPARSE>
+// RETRY: the second launch, over the rows listed by the first: workgroup (entry,
+// head, c) takes the listed rows 256 c .. 256 c + 255 (none: it returns at once).
+template <int D, int QB, int WAVES, int NST, bool ROPE, bool QK8, bool SPARSE, bool RETRY>
 __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   constexpr int KS = SPARSE ? 2 : 1;  // waves per query block (key split)
   constexpr int KH = 2 / KS;          // 32-key blocks per wave and tile
@@ -82,6 +88,7 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   static_assert(!SPARSE || (!QK8 && !ROPE && C::kBlockM == 64), "block-sparse: bfloat16, 64-query tiles");
   static_assert(NST == 4 || NST == 2, "stage count");
   static_assert(NST == 2 || WAVES % 2 == 0, "the wave offset pairs waves w and w + WAVES/2");
+  static_assert(!(RETRY && SPARSE) && (!RETRY || QB == 1), "row lists: dense, one query block per wave");
   // K and V^T stages, each its own array (not one array indexed by stage) so
   // that the compiler can tell a direct load into one stage from reads of
   // another and does not wait for the direct loads before LDS reads.
@@ -100,18 +107,26 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   __shared__ float ks_lds[QK8 ? (NST == 4 ? kQK8MaxTiles : kSmallKeys / kBlockN) : 1];
   // block-sparse: the key tiles this workgroup visits
   __shared__ uint16_t tile_lds[SPARSE ? kVsaMaxKeep : 1];
+  // retry launch: the query rows of the chunk in progress (-1 past the list)
+  __shared__ int row_lds[RETRY ? C::kBlockM : 1];
 
   // Workgroups are dispatched round-robin over the 8 XCDs; renumber them so that
   // each XCD walks a contiguous range of (head, query tile) and its L2 serves the
   // K/V tiles of one head to all its CUs.
-  const int nwg = gridDim.x;
-  const int wg = blockIdx.x;
-  const int xcd = wg & 7;
-  const int per = nwg >> 3;
-  const int rem = nwg & 7;
-  const int id = xcd * per + (xcd < rem ? xcd : rem) + (wg >> 3);
-  const int bh = id / a.n_qtiles;          // batch entry * hc + local head
-  const int qtile = id - bh * a.n_qtiles;
+  int bh, qtile;
+  if constexpr (RETRY) {
+    bh = blockIdx.x / a.n_qtiles;
+    qtile = blockIdx.x - bh * a.n_qtiles;      // chunk of the row list
+  } else {
+    const int nwg = gridDim.x;
+    const int wg = blockIdx.x;
+    const int xcd = wg & 7;
+    const int per = nwg >> 3;
+    const int rem = nwg & 7;
+    const int id = xcd * per + (xcd < rem ? xcd : rem) + (wg >> 3);
+    bh = id / a.n_qtiles;                    // batch entry * hc + local head
+    qtile = id - bh * a.n_qtiles;
+  }
   const int bat = bh / a.hc;
   const int head = bh - bat * a.hc;
 
@@ -125,15 +140,32 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
 
   if (tid == 0) wg_retry = 0;
 
+  // retry launch: the rows listed for this (entry, head), chunk qtile of them
+  int n_listed = 0;
+  if constexpr (RETRY) {
+    // written by the attention launch before this one: a plain (scalar) load sees it
+    n_listed = a.retry_cnt[2 * bh];
+    if (qtile * C::kBlockM >= n_listed) return;  // whole workgroup: nothing listed here
+    const int i = qtile * C::kBlockM + tid;
+    if (tid < C::kBlockM) row_lds[tid] = i < n_listed ? a.retry_rows[(int64_t)bh * a.nq + i] : -1;
+    __syncthreads();
+  }
+  // query row of row r of this wave (-1: none)
+  auto row_of = [&](int r) -> int {
+    if constexpr (RETRY)
+      return row_lds[qw * QB * 32 + r];
+    else
+      return qtile * C::kBlockM + qw * QB * 32 + r;
+  };
+
   // ---- this wave's queries into registers (B operand layout), RoPE fused
-  const int q0 = qtile * C::kBlockM + qw * QB * 32;
   QFrag qf[QB][C::kDK];
   float cq[QB];  // factor of the float scores in the exponent (log2 domain)
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int qi = q0 + qb * 32 + l32;
+    const int qi = row_of(qb * 32 + l32);
     cq[qb] = a.c;
-    if (qi < a.nq) {
+    if (qi >= 0 && qi < a.nq) {
       if constexpr (QK8) {
         // lane half h holds dims [32 kk + 16 h, 32 kk + 16 h + 16) of k-step kk
         const int8_t* qp = a.qc + bh * a.qc_bh + (int64_t)qi * D + 16 * hl;
@@ -489,11 +521,14 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   // stages) and form the scores of tile 0.
   f32x16 s_a[QB][KH], s_b[QB][KH];
   float c_a[QB], c_b[QB];
-  auto prologue = [&]() {
+  auto load_kscales = [&]() {
     if constexpr (QK8) {
       const float* ksrc = a.ksc + (int64_t)bh * a.nk_blocks;
       for (int i = tid; i < ntiles; i += C::kThreads) ks_lds[i] = ksrc[i];
     }
+  };
+  auto prologue = [&]() {
+    load_kscales();
     dma_k(0, k_st0);
     dma_v(0, v_st0);
     dma_k(1, k_st1);
@@ -624,32 +659,14 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
     }
   };
 
-  // ---- reference maximum from the first key tile
-  prologue();
-  float mref[QB];
-  tile_max(s_a, c_a, mref);
-  main_pass(mref);
-  // reference of the weights in o and l_run (the retry below replaces it)
-  float mfin[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) mfin[qb] = mref[qb];
-
-  // ---- rare path: some weight left the float16 range (a later key scored far
-  // above the first tile's maximum) or the inputs were not finite. The whole
-  // workgroup recomputes with the exact row maximum, so no weight exceeds 1.
-  bool bad = false;
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) bad |= !__builtin_isfinite(l_run[qb]);
-  if (__any(bad) && lane == 0) wg_retry = 1;
-  __syncthreads();
-  if (wg_retry) {
+  // exact row maximum: a q.k-only pass over every key tile
+  auto exact_max = [&](float (&mx)[QB]) {
     // recompute the staging addresses here instead of keeping the prologue's
     // across the main pass (which would cost registers or scratch there)
 #pragma unroll
     for (int i = 0; i < C::kKDma; ++i) asm volatile("" : "+v"(kdma_row[i]), "+v"(kdma_off[i]));
 #pragma unroll
     for (int i = 0; i < C::kVDma; ++i) asm volatile("" : "+v"(vdma_off[i]));
-    float mx[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) mx[qb] = -__builtin_inff();
     for (int t = 0; t < ntiles; ++t) {
@@ -666,10 +683,52 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
       for (int qb = 0; qb < QB; ++qb) mx[qb] = fmaxf(mx[qb], m[qb]);
       __syncthreads();
     }
+  };
+
+  // reference of the weights in o and l_run
+  float mfin[QB];
+  if constexpr (RETRY) {
+    // listed rows: the exact row maximum, so no weight exceeds 1
+    if constexpr (QK8) {
+      load_kscales();
+      __syncthreads();
+    }
+    exact_max(mfin);
     prologue();
-    main_pass(mx);
+    main_pass(mfin);
+  } else {
+    // ---- reference maximum from the first key tile
+    prologue();
+    tile_max(s_a, c_a, mfin);
+    main_pass(mfin);
+    // ---- rare path: some weight left the float16 range (a later key scored far
+    // above the first tile's maximum) or the inputs were not finite.
+    if constexpr (SPARSE) {
+      // the whole workgroup recomputes with the exact row maximum
+      bool bad = false;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) mfin[qb] = mx[qb];
+      for (int qb = 0; qb < QB; ++qb) bad |= !__builtin_isfinite(l_run[qb]);
+      if (__any(bad) && lane == 0) wg_retry = 1;
+      __syncthreads();
+      if (wg_retry) {
+        exact_max(mfin);
+        prologue();
+        main_pass(mfin);
+      }
+    } else {
+      // the rows go to the retry list of this (entry, head); the retry launch
+      // recomputes them (and overwrites what the epilogue below stores for them)
+      const int qi = row_of(l32);
+      const float lt = l_run[0] + __shfl_xor(l_run[0], 32);
+      const bool bad = hl == 0 && qi < a.nq && !__builtin_isfinite(lt);
+      const uint64_t m = __ballot(bad);
+      if (m != 0) {
+        int base = 0;
+        if (lane == 0) base = atomicAdd(a.retry_cnt + 2 * bh, __popcll(m));
+        base = __shfl(base, 0);
+        if (bad) a.retry_rows[(int64_t)bh * a.nq + base + __popcll(m & ((uint64_t(1) << lane) - 1))] = qi;
+      }
+    }
   }
 
   // ---- key split: the wave with the second key half hands its row sums,
@@ -771,23 +830,44 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
     for (int k = 0; k < 32 / kRowsPerStore; ++k) {
       const int row = k * kRowsPerStore + lane / kGran;
       const u32x4 v = *reinterpret_cast<const u32x4*>(stg + row * kRowBytes + (((2 * gi) ^ (2 * (row & (kGran - 1)))) << 3));
-      const int qi = q0 + row;
-      if (qi < a.nq) {
+      const int qi = row_of(row);
+      if (qi >= 0 && qi < a.nq) {
         __bf16* op = a.out + bat * a.out_batch + ((int64_t)qi * a.hc + head) * D + gi * 8;
         *reinterpret_cast<u32x4*>(op) = v;
       }
     }
   }
+
+  // retry launch: count the rows done; the workgroup that completes the list
+  // clears both counters for the next call (the prepare stage clears them too)
+  if constexpr (RETRY) {
+    if (tid == 0) {
+      const int n_done = min(C::kBlockM, n_listed - qtile * C::kBlockM);
+      const int before = atomicAdd(a.retry_cnt + 2 * bh + 1, n_done);
+      if (before + n_done == n_listed) {
+        atomicExch(a.retry_cnt + 2 * bh, 0);
+        atomicExch(a.retry_cnt + 2 * bh + 1, 0);
+      }
+    }
+  }
 }
 
+// The attention launch and, for the dense modes, the retry launch over the rows
+// whose float16 weights overflowed (usually none: its workgroups then only read
+// the row count and return), one workgroup per possible chunk of 256 rows.
 template <int D, int QB, int WAVES, int NST, bool ROPE, bool QK8, bool SPARSE = false>
 hipError_t launch_fwd_t(AttnArgs a, hipStream_t s) {
   using C = FwdCfg<D, QB, WAVES, QK8, SPARSE ? 2 : 1>;
   a.n_qtiles = (a.nq + C::kBlockM - 1) / C::kBlockM;
-  const int64_t nwg = (int64_t)a.n_qtiles * a.hc * a.batch;
+  const int64_t nbh = (int64_t)a.hc * a.batch;
+  const int64_t nwg = (int64_t)a.n_qtiles * nbh;
   if (nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, QB, WAVES, NST, ROPE, QK8, SPARSE>), dim3((unsigned)nwg), dim3(C::kThreads),
-                     0, s, a);
+  if (!SPARSE && (!a.retry_cnt || !a.retry_rows)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((attn_fwd_kernel<D, QB, WAVES, NST, ROPE, QK8, SPARSE, false>), dim3((unsigned)nwg),
+                     dim3(C::kThreads), 0, s, a);
+  if constexpr (!SPARSE)
+    hipLaunchKernelGGL((attn_fwd_kernel<D, QB, WAVES, NST, ROPE, QK8, false, true>), dim3((unsigned)nwg),
+                       dim3(C::kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -177,6 +177,10 @@ struct AttnArgs {
   const int32_t* tiles;
   int32_t keep;
   const int32_t* vexp;   // [bh]: v was scaled by 2^vexp before the float16 conversion
+  // rows whose float16 weights overflowed, per (entry, head): counters [bh][2]
+  // (rows listed, rows redone; zero between calls) and the rows [bh][nq]
+  int32_t* retry_cnt;
+  int32_t* retry_rows;
   int32_t kv_len[kMaxBatch];  // valid keys of each entry
 };
 
@@ -216,6 +220,7 @@ struct PrepArgs {
   RopeGeom rope;
   float* vpart;          // [bh][kVParts] partial maxima of |v|
   int32_t* vexp;         // [bh] exponent of the v scaling (written by key tile 0)
+  int32_t* retry_cnt;    // [bh][2] retry counters of the attention launch, cleared by key tile 0
   int32_t kv_len[kMaxBatch];
 };
 

@@ -81,7 +81,13 @@ __global__ void __launch_bounds__(256) prepare_kernel(PrepArgs a) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
   const int vsh = v_scale_exp(amax);
-  if (tile == 0 && tid == 0) a.vexp[bh] = vsh;
+  if (tile == 0 && tid == 0) {
+    a.vexp[bh] = vsh;
+    if (a.retry_cnt) {
+      a.retry_cnt[2 * bh] = 0;
+      a.retry_cnt[2 * bh + 1] = 0;
+    }
+  }
 
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) {

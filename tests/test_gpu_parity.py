@@ -91,7 +91,9 @@ def workspace_layout(B, hc, nq, nk, d, *, rope=False, int8=False):
         end = r["ks"] + s * (nk_pad // 64) * 4
     r["vpart"] = align256(end)
     r["vexp"] = align256(r["vpart"] + s * 64 * 4)
-    r["end"] = r["vexp"] + s * 4
+    r["retry_cnt"] = align256(r["vexp"] + s * 4)
+    r["retry_rows"] = align256(r["retry_cnt"] + s * 2 * 4)
+    r["end"] = r["retry_rows"] + s * nq * 4
     return r
 
 
@@ -581,3 +583,28 @@ def test_value_scale_ignores_masked_keys(dev):
     other = run_nhd(dev, q, k, v2, key_len=L)
     assert torch.equal(base.view(torch.int16), other.view(torch.int16))
     check(as_f64(base), oracle.mha_reference(q, k, v, key_len=L), "v scale 1e-5 masked", v_scale=1e-5)
+
+
+def test_retry_list_sparse_rows_and_repeated_attend(dev):
+    # 1% of the rows (at random) score far past their first key tile: only those
+    # rows are listed and recomputed by the retry launch. Two attends after one
+    # prepare give the same bits, and the list counters are zero after each.
+    vd = vdm()
+    n, ht = 4096, 16
+    q, k, v = nhd_inputs(n, n, ht, 128, 9950, 0.5)
+    hot = np.random.default_rng(9950).choice(n, size=n // 100, replace=False)
+    q[:, :, 0] = 0
+    q[hot, :, 0] = si.f32_to_bf16_bits(np.full((len(hot), ht), 8.0, dtype=np.float32))
+    k[:, :, 0] = si.f32_to_bf16_bits(np.broadcast_to((np.arange(n, dtype=np.float32) / 128.0)[:, None], (n, ht)))
+    note(f"retry list: {len(hot)} hot rows of {n}, {ht} heads")
+    attn = vd.Attention(n, n, ht, 128)
+    qd, kd, vd_ = up(q, dev), up(k, dev), up(v, dev)
+    ws = attn.prepare(qd, kd, vd_)
+    o1 = attn.attend(qd, kd, vd_, workspace=ws)
+    o2 = attn.attend(qd, kd, vd_, workspace=ws)
+    torch.cuda.synchronize()
+    lay = workspace_layout(1, ht, n, n, 128)
+    cnt = ws[lay["retry_cnt"]:lay["retry_cnt"] + ht * 8].view(torch.int32).cpu().numpy()
+    assert np.all(cnt == 0), cnt
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    check(as_f64(o1), oracle.mha_reference(q, k, v), "retry list 1% hot rows")
