@@ -19,10 +19,11 @@
 // each group of 16 permuted (bits 2 and 3 of the key index swapped) so that the
 // A operand for a lane is one 16-byte LDS read.
 //
-// Per iteration a wave forms the scores of the next tile while it turns the held
-// scores into weights, then runs the weight products. With four stages the two
-// waves sharing a SIMD are kept half an iteration apart (one forms scores and
-// weights while the other runs products).
+// Per iteration a wave forms the scores of the next tile while it turns half of
+// the held scores into weights, then runs the weight products while it turns the
+// other half of the next tile's scores into weights, so both phases carry the same
+// vector work. With four stages the two waves sharing a SIMD are kept half an
+// iteration apart (one forms scores while the other runs products).
 //
 // Block-sparse mode (SPARSE): the workgroup is one 64-query tile and visits only
 // the key tiles listed for it, in list order. Four waves split it: wave w takes
@@ -405,11 +406,31 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   // kR V^T fragments of the products in `vr`
   // `issue(g)` runs after score product g (the block-sparse mode issues its
   // direct loads there, one per product)
+  // SPLIT: the weights of a tile are formed half in the score phase (pairs
+  // kPairs/2 ..) and half in the product phase before it (pairs 0 .. kPairs/2 - 1,
+  // from the scores just formed), so both phases carry the same vector work.
+  constexpr bool SPLIT = KH == 2 && kNS == kPairs && kNP == kPairs;
+  constexpr int kHalf = kPairs / 2;
   auto score_phase = [&](const char* k_read, const char* v_read, const f32x16 (&s_cur)[QB][KH],
                          f32x16 (&s_next)[QB][KH], const float (&ccur)[QB], const float (&mref)[QB],
-                         f16x8 (&vr)[kR], f16x8 (&pf)[QB][2 * KH], f16x2 (&hv)[QB][kPairs], auto&& issue) {
+                         f16x8 (&vr)[kR], f16x8 (&pf)[QB][2 * KH], f16x2 (&hv)[QB][kPairs],
+                         const u32x4 (&wpre)[QB][KH], auto&& issue) {
     QFrag kr[kR];
     u32x4 bits[QB][2 * KH];
+    if constexpr (SPLIT) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int s4 = 0; s4 < KH; ++s4) {
+          bits[qb][s4] = wpre[qb][s4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            // through a local: a bit cast of a vector element read element 0
+            const uint32_t u = wpre[qb][s4][e];
+            hv[qb][s4 * 4 + e] = __builtin_bit_cast(f16x2, u);
+          }
+        }
+    }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -466,7 +487,7 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
     };
 #pragma unroll
     for (int j = 0; j < kR; ++j) kr[j] = kfrag(k_read, j);
-    form_x(0);
+    if constexpr (!SPLIT) form_x(0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int g = 0; g < kNS; ++g) {
@@ -479,12 +500,22 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
         kr[g % kR] = kfrag(k_read, g + kR);
       else
         vr[g + kR - kNS] = vfrag(v_read, g + kR - kNS);
-      if (g > 0) round_w(g - 1);
-      exp_x();
-      if (g + 1 < kNS) form_x(g + 1);
+      if constexpr (SPLIT) {
+        static_assert(kNS == 2 * kHalf, "one pair per two score products");
+        if (g % 2 == 0) {
+          if (g >= 2) round_w(kHalf / kPPG + g / 2 - 1);
+          form_x(kHalf / kPPG + g / 2);
+        } else {
+          exp_x();
+        }
+      } else {
+        if (g > 0) round_w(g - 1);
+        exp_x();
+        if (g + 1 < kNS) form_x(g + 1);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
-    round_w(kNS - 1);
+    round_w(SPLIT ? kHalf / kPPG + kNS / 2 - 1 : kNS - 1);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -495,7 +526,42 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   // with int8 q.k this also converts the integer scores of the next tile to
   // float, two per product
   auto product_phase = [&](const char* v_read, f16x8 (&vr)[kR], const f16x8 (&pf)[QB][2 * KH],
-                           const f16x2 (&hv)[QB][kPairs], f32x16 (&s_next)[QB][KH]) {
+                           const f16x2 (&hv)[QB][kPairs], f32x16 (&s_next)[QB][KH], const float (&cnext)[QB],
+                           const float (&mref)[QB], u32x4 (&wnext)[QB][KH]) {
+    // the first half of the next tile's weights, pair i: x at group 2i, 2^x at 2i+1,
+    // rounded at 2i+2
+    float xs[QB][2], es[QB][2];
+    auto form_n = [&](int i) {
+      const int s4 = i >> 2, e = i & 3;
+      const int skb = s4 >> 1, r = (s4 & 1) * 8 + 2 * e;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float nm = QK8 ? -__builtin_fmaf(kMagic, cnext[qb], mref[qb]) : -mref[qb];
+        xs[qb][0] = __builtin_fmaf(s_next[qb][skb][r], cnext[qb], nm);
+        xs[qb][1] = __builtin_fmaf(s_next[qb][skb][r + 1], cnext[qb], nm);
+        asm volatile("" : "+v"(xs[qb][0]), "+v"(xs[qb][1]));
+      }
+    };
+    auto exp_n = [&]() {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        es[qb][0] = __builtin_amdgcn_exp2f(xs[qb][0]);
+        es[qb][1] = __builtin_amdgcn_exp2f(xs[qb][1]);
+        asm volatile("" : "+v"(es[qb][0]), "+v"(es[qb][1]));
+      }
+    };
+    auto round_n = [&](int i) {
+      const int s4 = i >> 2, e = i & 3;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        f16x2 h2;
+        h2[0] = (_Float16)es[qb][0];
+        h2[1] = (_Float16)es[qb][1];
+        uint32_t u = __builtin_bit_cast(uint32_t, h2);
+        asm volatile("" : "+v"(u));
+        wnext[qb][s4][e] = u;
+      }
+    };
 #pragma unroll
     for (int g = 0; g < kNP; ++g) {
       const int s4 = g / C::kDB, db = g % C::kDB;
@@ -510,7 +576,34 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
           lpart[qb][p >> 2] = __builtin_amdgcn_fdot2(hv[qb][p], ones, lpart[qb][p >> 2], false);
           asm volatile("" : "+v"(lpart[qb][p >> 2]));  // keeps the sum in this group
         }
+      if constexpr (SPLIT) {
+        static_assert(kNP == 2 * kHalf, "one pair per two weight products");
+        if (g % 2 == 0) {
+          if (g >= 2) round_n(g / 2 - 1);
+          form_n(g / 2);
+        } else {
+          exp_n();
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (SPLIT) round_n(kHalf - 1);
+  };
+  // the first half of tile 0's weights (before the pipelined pass)
+  auto prime_weights = [&](const f32x16 (&s0)[QB][KH], const float (&c0)[QB], const float (&mref)[QB],
+                           u32x4 (&w)[QB][KH]) {
+#pragma unroll
+    for (int i = 0; i < kHalf; ++i) {
+      const int s4 = i >> 2, e = i & 3;
+      const int skb = s4 >> 1, r = (s4 & 1) * 8 + 2 * e;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float nm = QK8 ? -__builtin_fmaf(kMagic, c0[qb], mref[qb]) : -mref[qb];
+        f16x2 h2;
+        h2[0] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(s0[qb][skb][r], c0[qb], nm));
+        h2[1] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(s0[qb][skb][r + 1], c0[qb], nm));
+        w[qb][s4][e] = __builtin_bit_cast(uint32_t, h2);
+      }
     }
   };
 
@@ -579,7 +672,7 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   // c_cur / c_next: exponent factors of the scores held for tiles t and t+1
   auto step = [&](int t, char* k_read, char* k_fill, char* v_read, char* v_fill, f32x16 (&s_cur)[QB][KH],
                   f32x16 (&s_next)[QB][KH], const float (&c_cur)[QB], float (&c_next)[QB],
-                  const float (&mref)[QB]) {
+                  const float (&mref)[QB], const u32x4 (&w_cur)[QB][KH], u32x4 (&w_next)[QB][KH]) {
     f16x8 vr[kR];
     f16x8 pf[QB][2 * KH];
     f16x2 hv[QB][kPairs];
@@ -607,7 +700,7 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
       }
 #pragma unroll
       for (int i = 0; i < C::kVDma; ++i) ga[C::kKDma + i] = vt + vdma_off[i];
-      score_phase(k_read, v_read, s_cur, s_next, c_cur, mref, vr, pf, hv, [&](int g) {
+      score_phase(k_read, v_read, s_cur, s_next, c_cur, mref, vr, pf, hv, w_cur, [&](int g) {
         if (g % kEvery != 0) return;
         const int i = g / kEvery;
         if (i < C::kKDma)
@@ -618,12 +711,12 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
     } else {
       dma_v(t + NST / 2, v_fill);
       dma_k(t + NST, k_fill);
-      score_phase(k_read, v_read, s_cur, s_next, c_cur, mref, vr, pf, hv, [](int) {});
+      score_phase(k_read, v_read, s_cur, s_next, c_cur, mref, vr, pf, hv, w_cur, [](int) {});
     }
     if (upper) sync();
-    product_phase(v_read, vr, pf, hv, s_next);
     mask_tail(t + 1, s_next);
     tile_c(t + 1, c_next);
+    product_phase(v_read, vr, pf, hv, s_next, c_next, mref, w_next);
     if (!upper) sync();
   };
   auto main_pass = [&](const float (&mref)[QB]) {
@@ -634,17 +727,19 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int db = 0; db < C::kDB; ++db) o[qb][db] = f32x16{};
     }
+    u32x4 w_a[QB][KH], w_b[QB][KH];
+    if constexpr (SPLIT) prime_weights(s_a, c_a, mref, w_a);
     if constexpr (NST == 4) {
       for (int t = 0; t < ntiles; t += 4) {
-        step(t, k_st1, k_st0, v_st0, v_st2, s_a, s_b, c_a, c_b, mref);
-        if (t + 1 < ntiles) step(t + 1, k_st2, k_st1, v_st1, v_st3, s_b, s_a, c_b, c_a, mref);
-        if (t + 2 < ntiles) step(t + 2, k_st3, k_st2, v_st2, v_st0, s_a, s_b, c_a, c_b, mref);
-        if (t + 3 < ntiles) step(t + 3, k_st0, k_st3, v_st3, v_st1, s_b, s_a, c_b, c_a, mref);
+        step(t, k_st1, k_st0, v_st0, v_st2, s_a, s_b, c_a, c_b, mref, w_a, w_b);
+        if (t + 1 < ntiles) step(t + 1, k_st2, k_st1, v_st1, v_st3, s_b, s_a, c_b, c_a, mref, w_b, w_a);
+        if (t + 2 < ntiles) step(t + 2, k_st3, k_st2, v_st2, v_st0, s_a, s_b, c_a, c_b, mref, w_a, w_b);
+        if (t + 3 < ntiles) step(t + 3, k_st0, k_st3, v_st3, v_st1, s_b, s_a, c_b, c_a, mref, w_b, w_a);
       }
     } else {
       for (int t = 0; t < ntiles; t += 2) {
-        step(t, k_st1, k_st0, v_st0, v_st1, s_a, s_b, c_a, c_b, mref);
-        if (t + 1 < ntiles) step(t + 1, k_st0, k_st1, v_st1, v_st0, s_b, s_a, c_b, c_a, mref);
+        step(t, k_st1, k_st0, v_st0, v_st1, s_a, s_b, c_a, c_b, mref, w_a, w_b);
+        if (t + 1 < ntiles) step(t + 1, k_st0, k_st1, v_st1, v_st0, s_b, s_a, c_b, c_a, mref, w_b, w_a);
       }
     }
     // drain the direct loads still in flight before the stages are reused
