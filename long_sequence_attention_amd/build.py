@@ -49,6 +49,27 @@ def _scratch_users(asm: str) -> list[str]:
     return users
 
 
+_DMA = re.compile(r"^\s*global_load_lds_dwordx4\s+(\S+),\s*(\S+)")
+
+
+def _dma_hazards(asm: str) -> list[str]:
+    """Direct global->LDS loads written as inline assembly bypass the compiler's
+    hazard recognizer, so the build checks the form the kernels rely on: the
+    global address in a VGPR pair with no SGPR base ("off"), and the load
+    immediately preceded by an s_nop (the wait state after M0 is written)."""
+    bad = []
+    lines = asm.splitlines()
+    for i, line in enumerate(lines):
+        m = _DMA.match(line)
+        if not m:
+            continue
+        addr, base = m.group(1), m.group(2)
+        prev = lines[i - 1].strip() if i > 0 else ""
+        if not re.fullmatch(r"v\[\d+:\d+\]", addr) or base != "off" or not prev.startswith("s_nop"):
+            bad.append(f"line {i + 1}: {prev!r} / {line.strip()!r}")
+    return bad
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source into the shared library; returns its path."""
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
@@ -75,9 +96,14 @@ def build(verbose: bool = False) -> str:
                 sys.stderr.write(out + err)
                 raise RuntimeError(f"hipcc failed ({proc.returncode}) compiling {asm} for the scratch check")
             with open(asm) as f:
-                users = _scratch_users(f.read())
+                text = f.read()
+            users = _scratch_users(text)
             if users:
                 raise RuntimeError("kernels use scratch memory (spills or outlined helpers): " + "; ".join(users))
+            hazards = _dma_hazards(text)
+            if hazards:
+                raise RuntimeError(f"direct loads in {os.path.basename(asm)} not in the checked form: " +
+                                   "; ".join(hazards[:5]))
     os.replace(tmp, LIB)
     return LIB
 
