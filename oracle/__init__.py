@@ -24,7 +24,8 @@ Everything here is plain float64 numpy, written from the definitions:
     every code decided in float32 as the library decides it.
   * ``vsa``: block-sparse attention over 64-token tiles (the VSA kernels run at
     sparsity 0.8 with 64-token tiles on FastVideo's "Pair two NVIDIA DGX Sparks"
-    page), with the tile selection decided in float32 as the library decides it.
+    page): runs of 64 tokens, or 4 x 4 x 4 cubes of the latent grid, with the tile
+    selection decided in float32 as the library decides it.
 
 Parity status of each function is stated in its docstring.
 """

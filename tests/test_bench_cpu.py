@@ -44,7 +44,7 @@ def test_traffic_reported_only_for_the_measured_sources(tmp_path, monkeypatch):
 def test_committed_traffic_file_names_the_dominant_kernel():
     with open(os.path.join(ROOT, "profiles", "attn_fwd_n75600_h10_traffic.json")) as f:
         t = json.load(f)
-    assert t["kernel"].startswith("attn_fwd_kernel<128, 1, 8, 4, false, false, false>")
+    assert t["kernel"] == "attn_fwd_kernel<128, 1, 8, 4, false, false, false, false>"
     # bytes = FETCH_SIZE * calibration + WRITE_SIZE, in KiB (the stored scale is rounded)
     want = (t["fetch_kib_per_dispatch"] * t["fetch_scale"] + t["write_kib_per_dispatch"] * t["write_scale"]) * 1024
     assert abs(t["bytes_per_launch"] - want) <= 1e-5 * want

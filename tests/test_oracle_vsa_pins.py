@@ -9,7 +9,11 @@ other than itself:
     cut exceeds the float32 error bound;
   * keeping every tile reduces to the dense attention oracle;
   * brute force (explicit loops, math.exp) on tiny random inputs;
-  * permuting whole key tiles permutes the selection and leaves the output alone.
+  * permuting whole key tiles permutes the selection and leaves the output alone;
+  * cube tiles of a latent grid: hand-computed cube token lists, means, scores and
+    selections on a ragged grid (tests/golden/vsa_cube_selection.json), brute force
+    over grid coordinates, keep-all equal to dense attention, and whole cubes equal to
+    64-token tiles of the cube-ordered tokens.
 
 Mutations planted on the CPU (ties broken the other way, the ragged tile divided
 by 64, the query tile used as the key tile) show that the pins catch them.
@@ -186,6 +190,122 @@ def test_nan_scores_rank_lowest_and_negative_zero_ties():
     assert vsa.select_tiles(s, 4).tolist() == [[0, 1, 2, 3]]
 
 
+def cube_fixture():
+    with open(os.path.join(ROOT, "tests", "golden", "vsa_cube_selection.json")) as f:
+        return json.load(f)
+
+
+def cube_inputs(grid):
+    """q = (t, y, x, 1) and k = (2 [t = 4], 2 [y = 4], 0, w) per token, as bfloat16 bits [n, 1, 4]."""
+    T, H, W = grid
+    q = np.zeros((T * H * W, 1, 4), dtype=np.float32)
+    k = np.zeros_like(q)
+    for t in range(T):
+        for y in range(H):
+            for x in range(W):
+                n = (t * H + y) * W + x
+                q[n, 0] = (t, y, x, 1)
+                w = -6.0 if (t == 4 and y == 4) else x - 1.5
+                k[n, 0] = (2.0 if t == 4 else 0.0, 2.0 if y == 4 else 0.0, 0.0, w)
+    return si.f32_to_bf16_bits(q), si.f32_to_bf16_bits(k)
+
+
+def test_hand_cube_tokens_means_scores_and_selection():
+    fx = cube_fixture()
+    grid = tuple(fx["grid"])
+    cubes = vsa.cube_tiles(grid)
+    assert [c.tolist() for c in cubes] == fx["cube_tokens"]
+    q, k = cube_inputs(grid)
+    qm = vsa.group_means_f32(q[:, 0, :], cubes)
+    km = vsa.group_means_f32(k[:, 0, :], cubes)
+    assert qm.tolist() == fx["q_cube_means"]
+    assert km.tolist() == fx["k_cube_means"]
+    assert vsa.coarse_scores_f32(qm, km).tolist() == fx["coarse_scores"]
+    for keep, want in fx["selection"].items():
+        got = oracle.vsa_select(q, k, keep=int(keep), grid=grid)
+        assert got.shape == (1, 4, int(keep))
+        assert got[0].tolist() == want, f"keep={keep}"
+
+
+def test_cube_brute_force_ragged_grid():
+    """Grid 5 x 6 x 7 cuts cubes on all three sides (8 cubes of 64, 48, 32, 24, 16, 12,
+    8 and 6 tokens). Brute force: cube membership from each token's coordinates,
+    float32 means and scores one operation at a time, a sorted() selection, and the
+    fine stage with math.exp."""
+    grid = (5, 6, 7)
+    T, H, W = grid
+    n, d, keep = T * H * W, 8, 3
+    q = si.normal_bf16((n, 1, d), 2105, si.STREAM_Q)
+    k = si.normal_bf16((n, 1, d), 2105, si.STREAM_K)
+    v = si.normal_bf16((n, 1, d), 2105, si.STREAM_V)
+    qx, kx, vx = (oracle.bf16_bits_to_f64(a[:, 0, :]) for a in (q, k, v))
+    ncx, ncy = (W + 3) // 4, (H + 3) // 4
+    members = {}
+    for tok in range(n):
+        t, y, x = tok // (H * W), (tok // W) % H, tok % W
+        members.setdefault((t // 4 * ncy + y // 4) * ncx + x // 4, []).append(tok)
+    cubes = [members[c] for c in sorted(members)]
+    assert sorted(len(c) for c in cubes) == [6, 8, 12, 16, 24, 32, 48, 64]
+
+    def mean32(x, toks):
+        out = []
+        for c in range(d):
+            s = np.float32(0.0)
+            for tok in toks:
+                s = np.float32(s + np.float32(x[tok, c]))
+            out.append(np.float32(s / np.float32(len(toks))))
+        return out
+
+    qm = [mean32(qx, c) for c in cubes]
+    km = [mean32(kx, c) for c in cubes]
+    want_tiles = []
+    for i in range(len(cubes)):
+        sc = []
+        for j in range(len(cubes)):
+            s = np.float32(0.0)
+            for c in range(d):
+                s = np.float32(s + np.float32(qm[i][c] * km[j][c]))
+            sc.append(float(s))
+        want_tiles.append(sorted(sorted(range(len(cubes)), key=lambda j: (-sc[j], j))[:keep]))
+    rows = [0, 3, 27, 41, 100, 167, 168, 209]
+    out, tiles = oracle.vsa_reference(q, k, v, keep=keep, rows=rows, grid=grid)
+    assert tiles[0].tolist() == want_tiles
+    scale = 1.0 / math.sqrt(d)
+    cube_of = {tok: ci for ci, c in enumerate(cubes) for tok in c}
+    for r_i, r in enumerate(rows):
+        keys = [tok for j in want_tiles[cube_of[r]] for tok in cubes[j]]
+        s = [scale * sum(qx[r, c] * kx[j, c] for c in range(d)) for j in keys]
+        m = max(s)
+        w = [math.exp(x - m) for x in s]
+        want = [sum(wi * vx[j, c] for wi, j in zip(w, keys)) / sum(w) for c in range(d)]
+        assert np.allclose(out[r_i, 0], want, rtol=1e-12, atol=1e-14), r
+
+
+def test_cube_keep_all_is_dense_attention():
+    grid = (3, 5, 9)
+    n = 3 * 5 * 9
+    q = si.normal_bf16((n, 2, 16), 2106, si.STREAM_Q)
+    k = si.normal_bf16((n, 2, 16), 2106, si.STREAM_K)
+    v = si.normal_bf16((n, 2, 16), 2106, si.STREAM_V)
+    out, tiles = oracle.vsa_reference(q, k, v, sparsity=0.0, grid=grid)
+    assert tiles.shape == (2, 6, 6) and (tiles == np.arange(6)).all()
+    assert np.allclose(out, oracle.mha_reference(q, k, v), rtol=1e-12, atol=1e-14)
+
+
+def test_whole_cubes_are_64_token_tiles_in_cube_order():
+    grid = (8, 4, 8)
+    n = 256
+    q = si.normal_bf16((n, 1, 32), 2107, si.STREAM_Q)
+    k = si.normal_bf16((n, 1, 32), 2107, si.STREAM_K)
+    v = si.normal_bf16((n, 1, 32), 2107, si.STREAM_V)
+    perm = np.concatenate(vsa.cube_tiles(grid))
+    assert sorted(perm.tolist()) == list(range(n)) and perm.tolist() != list(range(n))
+    out_c, tiles_c = oracle.vsa_reference(q, k, v, keep=2, grid=grid)
+    out_r, tiles_r = oracle.vsa_reference(q[perm], k[perm], v[perm], keep=2)
+    assert tiles_c.tolist() == tiles_r.tolist()
+    assert np.array_equal(out_c[perm], out_r)
+
+
 # ---- planted mistakes: each must fail a pin above
 
 def test_mutation_ties_to_higher_index_is_caught(monkeypatch):
@@ -202,23 +322,35 @@ def test_mutation_ties_to_higher_index_is_caught(monkeypatch):
 
 
 def test_mutation_ragged_tile_divided_by_64_is_caught(monkeypatch):
-    def means_64(x_bits, tile=64):
+    def means_64(x_bits, groups):
         x = oracle.bf16_bits_to_f64(x_bits).astype(np.float32)
-        nt = (x.shape[0] + tile - 1) // tile
-        pad = np.zeros((nt * tile, x.shape[1]), dtype=np.float32)
-        pad[:x.shape[0]] = x
-        return pad.reshape(nt, tile, -1).sum(axis=1, dtype=np.float32) / np.float32(tile)
-    monkeypatch.setattr(vsa, "tile_means_f32", means_64)
+        return np.stack([x[g].sum(axis=0, dtype=np.float32) / np.float32(64) for g in groups])
+    monkeypatch.setattr(vsa, "group_means_f32", means_64)
     with pytest.raises(AssertionError):
         test_hand_means_scores_and_selection()
+    with pytest.raises(AssertionError):
+        test_hand_cube_tokens_means_scores_and_selection()
 
 
 def test_mutation_query_tile_as_key_tile_is_caught(monkeypatch):
     real = vsa.sparse_rows
 
-    def wrong(q, k, v, scale, q_tiles, tiles):
+    def wrong(q, k, v, scale, q_tiles, tiles, key_groups=None):
         diag = np.stack([np.full(tiles.shape[1], t) for t in range(tiles.shape[0])])
-        return real(q, k, v, scale, q_tiles, np.minimum(diag, (k.shape[0] - 1) // 64))
+        return real(q, k, v, scale, q_tiles, np.minimum(diag, (k.shape[0] - 1) // 64), key_groups)
     monkeypatch.setattr(vsa, "sparse_rows", wrong)
     with pytest.raises(AssertionError):
         test_brute_force_tiny()
+
+
+def test_mutation_cubes_numbered_ct_fastest_is_caught(monkeypatch):
+    real = vsa.cube_tiles
+
+    def transposed(grid):
+        cubes = real(grid)
+        T, H, W = (int(g) for g in grid)
+        nct, ncy, ncx = (T + 3) // 4, (H + 3) // 4, (W + 3) // 4
+        return [cubes[(ct * ncy + cy) * ncx + cx] for cx in range(ncx) for cy in range(ncy) for ct in range(nct)]
+    monkeypatch.setattr(vsa, "cube_tiles", transposed)
+    with pytest.raises(AssertionError):
+        test_hand_cube_tokens_means_scores_and_selection()
