@@ -101,7 +101,9 @@ typedef enum {
  *   scale           softmax scale; <= 0 selects 1/sqrt(d); NaN or inf is rejected
  *   use_key_mask    0: all nk keys; 1: only keys j < key_len (key_len given per call)
  *   use_rope        1: rotate q and k by the 3D RoPE above (requires nq == nk)
- *   grid_t/h/w      latent grid, grid_t * grid_h * grid_w == nq (used iff use_rope)
+ *   grid_t/h/w      latent grid, grid_t * grid_h * grid_w == nq, token n at
+ *                   t = n / (grid_h grid_w), y = (n / grid_w) % grid_h, x = n % grid_w
+ *                   (used iff use_rope or vsa_cubes)
  *   rope_dim_t/h/w  band widths, each even and > 0, summing to d (used iff use_rope)
  *   rope_base       base of the frequencies, > 0 and finite (used iff use_rope)
  *   batch           B, sequences per call (0 is read as 1; at most 64, and B * head_count
@@ -122,6 +124,10 @@ typedef enum {
  *                   q codes int8 [B * head_count][ceil(nq/128)*128][d], k codes int8
  *                   [B * head_count][ceil(nk/64)*64][d], q scales float
  *                   [B * head_count][ceil(nq/128)], k scales float [B * head_count][ceil(nk/64)].
+ *   vsa_cubes       1: the block-sparse calls (vdit_vsa_*) tile q and k as 4 x 4 x 4
+ *                   cubes of the latent grid instead of runs of 64 tokens (see there);
+ *                   needs nq == nk == grid_t * grid_h * grid_w and at most 8192 cubes
+ *                   (UNSUPPORTED beyond). The dense calls ignore it.
  */
 typedef struct {
   int32_t nq;
@@ -139,6 +145,7 @@ typedef struct {
   double rope_base;
   int32_t batch;
   int32_t qk_int8;
+  int32_t vsa_cubes;
 } vdit_attn_desc_t;
 
 /*
@@ -173,7 +180,10 @@ vdit_status_t vdit_attn_destroy(vdit_attn_t h);
  * Bytes of caller-provided device workspace that prepare/attend/fwd need for the
  * largest key length of this plan: v transposed to float16 per entry and head
  * ([B][head_count][ceil(nk/64)*64][d], 2 bytes) and, with use_rope, the rotated keys
- * (same shape, bfloat16), then the qk_int8 regions (above), then the range of v:
+ * (same shape, bfloat16); with vsa_cubes both regions are present and sized for
+ * max(ceil(nk/64), cubes) 64-key tiles per entry and head (the block-sparse calls
+ * lay them out [B][head_count][cubes * 64][d], v transposed and k in cube order);
+ * then the qk_int8 regions (above), then the range of v:
  * float [B][head_count][64] partial maxima of |v| and int32 [B][head_count] scaling
  * exponents e; then the retry list of the rows whose float16 weights overflowed:
  * int32 [B][head_count][2] counters (cleared by prepare, zero again after attend)
@@ -288,9 +298,15 @@ vdit_status_t vdit_attn_rope_probe(vdit_attn_t h, int32_t* idx_out, void* hip_st
  *
  *   tiles      runs of 64 consecutive tokens as the tensors hold them (the last
  *              one shorter if n is not a multiple of 64); Tq = ceil(nq/64) query
- *              tiles, Tk = ceil(nk/64) key tiles. A caller that wants tiles to
- *              be 4x4x4 cubes of the latent grid orders the tokens that way first.
- *   coarse     mean of each tile of q and of k (float32 sum in token order, then
+ *              tiles, Tk = ceil(nk/64) key tiles. With vsa_cubes, 4 x 4 x 4 cubes
+ *              of the latent grid (as in the published method): cube (ct, cy, cx)
+ *              holds the tokens with t/4 = ct, y/4 = cy, x/4 = cx; cubes are
+ *              numbered cx fastest, then cy, then ct; Tq = Tk = ceil(grid_t/4) *
+ *              ceil(grid_h/4) * ceil(grid_w/4). A grid side that is not a multiple
+ *              of 4 makes its last cubes thinner (1 to 64 tokens): such a cube is a
+ *              tile of its own tokens only (its mean divides by its token count,
+ *              its keys are its tokens).
+ *   coarse     mean of each tile of q and of k (float32 sum in ascending token order, then
  *              divided by the tile's token count); score(i, j) = sum over c of
  *              mean_q(i)[c] * mean_k(j)[c], each product and partial sum rounded
  *              to float32, c ascending (the positive softmax scale ranks nothing
@@ -309,7 +325,8 @@ vdit_status_t vdit_attn_rope_probe(vdit_attn_t h, int32_t* idx_out, void* hip_st
  *
  * vdit_vsa_keep: keep for a sparsity in [0, 1) (INVALID_ARG otherwise). Host only.
  * vdit_vsa_workspace_bytes: workspace bytes that every vsa call accepts for this
- *   keep: the attention workspace (v transposed), then the kept tiles
+ *   keep: the attention workspace (v transposed; with vsa_cubes also k, both in
+ *   cube order, one 64-slot tile per cube), then the kept tiles
  *   (int32 [B][head_count][Tq][keep]), the tile means (float32 [B][head_count][Tq][d]
  *   and [B][head_count][Tk][d]) and the coarse scores (float32
  *   [B][head_count][Tq][Tk]), each region 256-byte aligned. Host only.

@@ -23,7 +23,7 @@ class Desc(ctypes.Structure):
         ("use_rope", ctypes.c_int32), ("grid_t", ctypes.c_int32), ("grid_h", ctypes.c_int32),
         ("grid_w", ctypes.c_int32), ("rope_dim_t", ctypes.c_int32), ("rope_dim_h", ctypes.c_int32),
         ("rope_dim_w", ctypes.c_int32), ("rope_base", ctypes.c_double), ("batch", ctypes.c_int32),
-        ("qk_int8", ctypes.c_int32),
+        ("qk_int8", ctypes.c_int32), ("vsa_cubes", ctypes.c_int32),
     ]
 
 

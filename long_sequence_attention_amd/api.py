@@ -62,7 +62,8 @@ def ulysses_heads(heads_total: int, degree: int, rank: int) -> tuple[int, int]:
 
 def make_desc(nq: int, nk: int, heads_total: int, head_dim: int, *, layout: str = "NHD", head_begin: int = 0,
               head_count: int | None = None, scale: float = 0.0, use_key_mask: bool = False,
-              rope: dict | None = None, batch: int = 1, qk_int8: bool = False) -> _lib.Desc:
+              rope: dict | None = None, batch: int = 1, qk_int8: bool = False,
+              vsa_cubes: tuple | None = None) -> _lib.Desc:
     d = _lib.Desc()
     d.batch = batch
     d.qk_int8 = 1 if qk_int8 else 0
@@ -77,6 +78,9 @@ def make_desc(nq: int, nk: int, heads_total: int, head_dim: int, *, layout: str 
         d.grid_t, d.grid_h, d.grid_w = (int(g) for g in rope["grid"])
         d.rope_dim_t, d.rope_dim_h, d.rope_dim_w = (int(x) for x in rope["dims"])
         d.rope_base = float(rope.get("base", 10000.0))
+    if vsa_cubes is not None:
+        d.vsa_cubes = 1
+        d.grid_t, d.grid_h, d.grid_w = (int(g) for g in vsa_cubes)
     return d
 
 
@@ -92,17 +96,20 @@ class Attention:
 
     With ``batch`` = B > 1 every tensor has a leading [B] dimension; the calls take
     either one ``key_len`` for all entries or ``key_lens`` (B values). ``qk_int8``
-    selects q.k on int8 per-block codes (d = 128, no RoPE).
+    selects q.k on int8 per-block codes (d = 128, no RoPE). ``vsa_cubes`` = (T, H, W):
+    the block-sparse calls tile q and k as 4x4x4 cubes of that latent grid instead of
+    runs of 64 tokens.
     """
 
     def __init__(self, nq: int, nk: int, heads_total: int, head_dim: int, *, layout: str = "NHD",
                  head_begin: int = 0, head_count: int | None = None, scale: float = 0.0,
                  use_key_mask: bool = False, rope: dict | None = None, batch: int = 1,
-                 qk_int8: bool = False):
+                 qk_int8: bool = False, vsa_cubes: tuple | None = None):
         self._lib = _lib.load()
         self.desc = make_desc(nq, nk, heads_total, head_dim, layout=layout, head_begin=head_begin,
                               head_count=head_count, scale=scale, use_key_mask=use_key_mask, rope=rope,
-                              batch=batch, qk_int8=qk_int8)
+                              batch=batch, qk_int8=qk_int8, vsa_cubes=vsa_cubes)
+        self.vsa_cubes = None if vsa_cubes is None else tuple(int(g) for g in vsa_cubes)
         self.layout = layout
         self.batch = int(batch)
         h = ctypes.c_void_p()
@@ -213,14 +220,18 @@ class Attention:
                                                    _ptr(workspace), nbytes, sp), "vdit_attn_attend_lens")
         return out
 
-    # -- block-sparse attention over 64-token tiles (vdit_vsa_*)
+    # -- block-sparse attention over 64-token tiles or latent-grid cubes (vdit_vsa_*)
+    def _cubes(self) -> int:
+        t, h, w = self.vsa_cubes
+        return ((t + 3) // 4) * ((h + 3) // 4) * ((w + 3) // 4)
+
     @property
     def q_tiles(self) -> int:
-        return (self.desc.nq + 63) // 64
+        return self._cubes() if self.vsa_cubes else (self.desc.nq + 63) // 64
 
     @property
     def k_tiles(self) -> int:
-        return (self.desc.nk + 63) // 64
+        return self._cubes() if self.vsa_cubes else (self.desc.nk + 63) // 64
 
     def vsa_keep(self, sparsity: float) -> int:
         """Key tiles kept per query tile at ``sparsity``: ceil((1 - sparsity) * Tk), >= 1."""

@@ -17,6 +17,9 @@ struct vdit_attn {
   float c;             // scale * log2(e)
   int device;
   int64_t nk_pad;      // keys rounded up to the key tile
+  // block-sparse tiles as latent-grid cubes (vsa_cubes): one 64-slot tile per cube
+  vdit::CubeGeom cube;
+  int64_t vt_slots;    // key slots per (entry, head) of the V^T and k-copy regions
   size_t ws_vt_off, ws_vt_bytes;
   size_t ws_kr_off, ws_kr_bytes;
   // int8 q.k: codes and scales per (entry, head)
@@ -79,6 +82,14 @@ vdit_status_t validate_desc(const vdit_attn_desc_t& d) {
   if (row > (int64_t(1) << 40) || batch * nmax * row > (int64_t(1) << 60)) return VDIT_ERR_INVALID_ARG;
   // the kernels address a 64-key tile's rows with 32-bit byte offsets (row * stride * 2)
   if (int64_t(vdit::kBlockN) * row * 2 >= (int64_t(1) << 31)) return VDIT_ERR_UNSUPPORTED;
+  if (d.vsa_cubes != 0 && d.vsa_cubes != 1) return VDIT_ERR_INVALID_ARG;
+  if (d.vsa_cubes) {
+    if (d.nq != d.nk) return VDIT_ERR_INVALID_ARG;
+    if (d.grid_t < 1 || d.grid_h < 1 || d.grid_w < 1) return VDIT_ERR_INVALID_ARG;
+    if ((int64_t)d.grid_t * d.grid_h * d.grid_w != d.nq) return VDIT_ERR_INVALID_ARG;
+    const int64_t cubes = (int64_t)((d.grid_t + 3) / 4) * ((d.grid_h + 3) / 4) * ((d.grid_w + 3) / 4);
+    if (cubes > vdit::kVsaMaxTiles) return VDIT_ERR_UNSUPPORTED;
+  }
   if (d.use_rope) {
     if (d.nq != d.nk) return VDIT_ERR_INVALID_ARG;
     if (d.grid_t < 1 || d.grid_h < 1 || d.grid_w < 1) return VDIT_ERR_INVALID_ARG;
@@ -200,7 +211,9 @@ vdit_status_t check_call(const vdit_attn& h, void* workspace, size_t ws_bytes) {
   return VDIT_OK;
 }
 
-vdit_status_t do_prepare(const vdit_attn& h, const Inputs& in, const KeyLens& kl, void* ws, hipStream_t s) {
+// cubes: V^T and the k copy in cube order (block-sparse attention over cube tiles)
+vdit_status_t do_prepare(const vdit_attn& h, const Inputs& in, const KeyLens& kl, void* ws, hipStream_t s,
+                         bool cubes = false) {
   const vdit_attn_desc_t& d = h.desc;
   vdit::PrepArgs a{};
   a.k = in.k;
@@ -220,7 +233,14 @@ vdit_status_t do_prepare(const vdit_attn& h, const Inputs& in, const KeyLens& kl
   a.vexp = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + h.ws_vexp_off);
   a.retry_cnt = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + h.ws_rcnt_off);
   for (int32_t b = 0; b < vdit::kMaxBatch; ++b) a.kv_len[b] = kl.len[b];
-  if (vdit::launch_prepare(a, d.head_dim, d.use_rope != 0, s) != hipSuccess) return VDIT_ERR_DEVICE;
+  if (cubes) {
+    a.cube = h.cube;
+    a.n_ktiles = h.cube.n;
+    a.vt_head = h.vt_slots * d.head_dim;
+    a.kr = reinterpret_cast<__bf16*>(static_cast<char*>(ws) + h.ws_kr_off);
+    a.kr_head = h.vt_slots * d.head_dim;
+  }
+  if (vdit::launch_prepare(a, d.head_dim, d.use_rope != 0 && !cubes, s) != hipSuccess) return VDIT_ERR_DEVICE;
   if (d.qk_int8) {
     char* w = static_cast<char*>(ws);
     vdit::QuantArgs qa{};
@@ -347,12 +367,25 @@ vdit_status_t vdit_attn_create(const vdit_attn_desc_t* desc, vdit_attn_t* out) {
   h.scale = (float)scale;
   h.c = (float)(scale * 1.4426950408889634);  // log2(e)
   h.nk_pad = ((int64_t)d.nk + vdit::kBlockN - 1) / vdit::kBlockN * vdit::kBlockN;
-  const size_t per_head = (size_t)h.nk_pad * d.head_dim * 2;
+  h.cube = vdit::CubeGeom{};
+  if (d.vsa_cubes) {
+    h.cube.on = 1;
+    h.cube.t = d.grid_t;
+    h.cube.h = d.grid_h;
+    h.cube.w = d.grid_w;
+    h.cube.nct = (d.grid_t + vdit::kCube - 1) / vdit::kCube;
+    h.cube.ncy = (d.grid_h + vdit::kCube - 1) / vdit::kCube;
+    h.cube.ncx = (d.grid_w + vdit::kCube - 1) / vdit::kCube;
+    h.cube.n = h.cube.nct * h.cube.ncy * h.cube.ncx;
+  }
+  h.vt_slots = h.nk_pad;
+  if (d.vsa_cubes && (int64_t)h.cube.n * vdit::kBlockN > h.vt_slots) h.vt_slots = (int64_t)h.cube.n * vdit::kBlockN;
+  const size_t per_head = (size_t)h.vt_slots * d.head_dim * 2;
   h.ws_vt_off = 0;
   h.ws_vt_bytes = per_head * d.head_count * d.batch;
   h.ws_kr_off = align_up(h.ws_vt_bytes, 256);
-  h.ws_kr_bytes = d.use_rope ? per_head * d.head_count * d.batch : 0;
-  h.ws_total = d.use_rope ? h.ws_kr_off + h.ws_kr_bytes : h.ws_vt_bytes;
+  h.ws_kr_bytes = (d.use_rope || d.vsa_cubes) ? per_head * d.head_count * d.batch : 0;
+  h.ws_total = h.ws_kr_bytes ? h.ws_kr_off + h.ws_kr_bytes : h.ws_vt_bytes;
   h.nq_pad = ((int64_t)d.nq + vdit::kQuantQ - 1) / vdit::kQuantQ * vdit::kQuantQ;
   if (d.qk_int8) {
     const size_t slices = (size_t)d.head_count * d.batch;
@@ -540,13 +573,17 @@ struct VsaLayout {
 
 int32_t tiles_of(int32_t n) { return (n + vdit::kBlockN - 1) / vdit::kBlockN; }
 
+// query (= key) tiles of the block-sparse calls: runs of 64 tokens or cubes
+int32_t vsa_q_tiles(const vdit_attn& h) { return h.cube.on ? h.cube.n : tiles_of(h.desc.nq); }
+int32_t vsa_k_tiles(const vdit_attn& h) { return h.cube.on ? h.cube.n : tiles_of(h.desc.nk); }
+
 // Workspace: the attention part (transposed v), then the kept tiles (vdit_vsa_fwd),
 // the tile means of q and k and the coarse scores, each 256-byte aligned.
 VsaLayout vsa_layout(const vdit_attn& h, int32_t keep) {
   const vdit_attn_desc_t& d = h.desc;
   VsaLayout l{};
-  l.tq = tiles_of(d.nq);
-  l.tk = tiles_of(d.nk);
+  l.tq = vsa_q_tiles(h);
+  l.tk = vsa_k_tiles(h);
   const size_t bh = (size_t)d.batch * d.head_count;
   l.tiles_off = align_up(h.ws_total, 256);
   l.qm_off = align_up(l.tiles_off + bh * l.tq * (size_t)keep * sizeof(int32_t), 256);
@@ -560,7 +597,7 @@ vdit_status_t vsa_check(const vdit_attn* h, int32_t keep) {
   if (!is_live(h)) return VDIT_ERR_INVALID_ARG;
   const vdit_attn_desc_t& d = h->desc;
   if (d.use_key_mask || d.use_rope || d.qk_int8) return VDIT_ERR_UNSUPPORTED;
-  const int32_t tk = tiles_of(d.nk);
+  const int32_t tk = vsa_k_tiles(*h);
   if (tk > vdit::kVsaMaxTiles) return VDIT_ERR_UNSUPPORTED;
   if (keep < 1 || keep > tk) return VDIT_ERR_INVALID_ARG;
   if (keep > vdit::kVsaMaxKeep) return VDIT_ERR_UNSUPPORTED;
@@ -594,6 +631,7 @@ vdit_status_t do_vsa_select(const vdit_attn& h, const Inputs& in, const VsaLayou
   m.mean = reinterpret_cast<float*>(w + l.qm_off);
   m.n = d.nq;
   m.tiles = l.tq;
+  m.cube = h.cube;
   if (vdit::launch_vsa_means(m, d.head_dim, s) != hipSuccess) return VDIT_ERR_DEVICE;
   m.x = in.k;
   m.row = in.kv_row;
@@ -622,18 +660,28 @@ vdit_status_t do_vsa_attend(const vdit_attn& h, const Inputs& in, int32_t keep, 
   KeyLens kl;
   vdit_status_t st = resolve_lens(h, false, 0, nullptr, kl);
   if (st != VDIT_OK) return st;
-  if ((st = do_prepare(h, in, kl, ws, s)) != VDIT_OK) return st;
+  const bool cubes = h.cube.on != 0;
+  if ((st = do_prepare(h, in, kl, ws, s, cubes)) != VDIT_OK) return st;
   vdit::AttnArgs a{};
   a.q = in.q;
   a.q_row = in.q_row;
   a.q_head = d.head_dim;
   a.q_batch = in.q_batch;
-  a.k = in.k;
-  a.k_row = in.kv_row;
-  a.k_head = d.head_dim;
-  a.k_batch = in.kv_batch;
+  if (cubes) {
+    // k in cube order from the workspace, every cube one 64-slot key tile
+    a.k = reinterpret_cast<const __bf16*>(static_cast<const char*>(ws) + h.ws_kr_off);
+    a.k_row = d.head_dim;
+    a.k_head = h.vt_slots * d.head_dim;
+    a.k_batch = a.k_head * d.head_count;
+    a.cube = h.cube;
+  } else {
+    a.k = in.k;
+    a.k_row = in.kv_row;
+    a.k_head = d.head_dim;
+    a.k_batch = in.kv_batch;
+  }
   a.vt = reinterpret_cast<const _Float16*>(static_cast<const char*>(ws) + h.ws_vt_off);
-  a.vt_head = h.nk_pad * d.head_dim;
+  a.vt_head = (cubes ? h.vt_slots : h.nk_pad) * d.head_dim;
   a.vt_batch = a.vt_head * d.head_count;
   a.out = static_cast<__bf16*>(out);
   a.out_batch = (int64_t)d.nq * d.head_count * d.head_dim;
@@ -644,7 +692,8 @@ vdit_status_t do_vsa_attend(const vdit_attn& h, const Inputs& in, int32_t keep, 
   a.tiles = tiles;
   a.keep = keep;
   a.vexp = reinterpret_cast<const int32_t*>(static_cast<const char*>(ws) + h.ws_vexp_off);
-  for (int32_t b = 0; b < vdit::kMaxBatch; ++b) a.kv_len[b] = kl.len[b];
+  for (int32_t b = 0; b < vdit::kMaxBatch; ++b)
+    a.kv_len[b] = cubes && b < d.batch ? (int32_t)(h.cube.n * vdit::kBlockN) : kl.len[b];
   if (vdit::launch_attn_sparse(a, d.head_dim, s) != hipSuccess) return VDIT_ERR_DEVICE;
   return VDIT_OK;
 }
@@ -656,7 +705,7 @@ extern "C" {
 vdit_status_t vdit_vsa_keep(vdit_attn_t h, double sparsity, int32_t* keep) {
   if (!is_live(h) || !keep) return VDIT_ERR_INVALID_ARG;
   if (!(sparsity >= 0.0 && sparsity < 1.0)) return VDIT_ERR_INVALID_ARG;
-  const int32_t tk = tiles_of(h->desc.nk);
+  const int32_t tk = vsa_k_tiles(*h);
   const double want = std::ceil((1.0 - sparsity) * (double)tk);
   *keep = want < 1.0 ? 1 : (want > (double)tk ? tk : (int32_t)want);
   return VDIT_OK;
@@ -704,7 +753,7 @@ vdit_status_t vdit_vsa_attend(vdit_attn_t h, const void* q, const void* k, const
   if (!aligned16(workspace)) return VDIT_ERR_ALIGNMENT;
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev != h->device) return VDIT_ERR_DEVICE;
-  const size_t tb = (size_t)h->desc.batch * h->desc.head_count * tiles_of(h->desc.nq) * keep * sizeof(int32_t);
+  const size_t tb = (size_t)h->desc.batch * h->desc.head_count * vsa_q_tiles(*h) * keep * sizeof(int32_t);
   const size_t ob = (size_t)h->desc.batch * h->desc.nq * h->desc.head_count * h->desc.head_dim * 2;
   if (ws_overlaps_inputs(in, workspace, h->ws_total) || overlaps(tiles, tb, workspace, h->ws_total) ||
       overlaps(tiles, tb, out, ob))

@@ -106,8 +106,11 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   __shared__ int wg_retry;
   // int8 q.k: k scale of every key tile of this (entry, head), copied in the prologue
   __shared__ float ks_lds[QK8 ? (NST == 4 ? kQK8MaxTiles : kSmallKeys / kBlockN) : 1];
-  // block-sparse: the key tiles this workgroup visits
+  // block-sparse: the key tiles this workgroup visits (with cube tiles, bits 13-15
+  // mark the last cube along t, y and x, whose token counts are fixed)
   __shared__ uint16_t tile_lds[SPARSE ? kVsaMaxKeep : 1];
+  // block-sparse cube tiles: the two waves of a query block exchange their references
+  __shared__ float ref_lds[SPARSE ? WAVES * 32 : 1];
   // retry launch: the query rows of the chunk in progress (-1 past the list)
   __shared__ int row_lds[RETRY ? C::kBlockM : 1];
 
@@ -151,12 +154,21 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
     if (tid < C::kBlockM) row_lds[tid] = i < n_listed ? a.retry_rows[(int64_t)bh * a.nq + i] : -1;
     __syncthreads();
   }
+  // block-sparse cube tiles: the query tile is cube qtile
+  Cube qcube{};
+  if constexpr (SPARSE)
+    if (a.cube.on) qcube = cube_at(a.cube, qtile);
   // query row of row r of this wave (-1: none)
   auto row_of = [&](int r) -> int {
-    if constexpr (RETRY)
+    if constexpr (RETRY) {
       return row_lds[qw * QB * 32 + r];
-    else
+    } else {
+      if constexpr (SPARSE) {
+        const int slot = qw * QB * 32 + r;
+        if (a.cube.on) return slot < qcube.len ? cube_token(a.cube, qcube, slot) : -1;
+      }
       return qtile * C::kBlockM + qw * QB * 32 + r;
+    }
   };
 
   // ---- this wave's queries into registers (B operand layout), RoPE fused
@@ -196,14 +208,19 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   if constexpr (SPARSE) {
     // tile indices out of range are clamped, so every load stays in bounds
     const int32_t* lst = a.tiles + ((int64_t)bh * a.n_qtiles + qtile) * a.keep;
-    for (int i = tid; i < ntiles; i += C::kThreads) tile_lds[i] = (uint16_t)min(max(lst[i], 0), ktiles - 1);
+    static_assert(kVsaMaxTiles <= (1 << 13), "tile indices below bit 13");
+    for (int i = tid; i < ntiles; i += C::kThreads) {
+      const int j = min(max(lst[i], 0), ktiles - 1);
+      const int fl = a.cube.on ? cube_at(a.cube, j).flags : 0;
+      tile_lds[i] = (uint16_t)(j | (fl << 13));
+    }
     __syncthreads();
   }
   // key tile of visit t; visits past the last one repeat it
   auto tile_of = [&](int t) -> int {
     t = min(t, ntiles - 1);
     if constexpr (SPARSE)
-      return tile_lds[t];
+      return tile_lds[t] & 0x1fff;
     else
       return t;
   };
@@ -333,15 +350,27 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   };
   // scores of keys past kv_len to -inf (only the last key tile can hold such keys)
   const bool ragged = (kv_len & (kBlockN - 1)) != 0;
+  // (block-sparse: the ragged last tile, or a cube of fewer than 64 tokens)
   auto mask_tail = [&](int t, f32x16 (&s)[QB][KH]) {
-    const bool last = SPARSE ? t < ntiles && tile_of(t) == ktiles - 1 : t == ntiles - 1;
-    if (last && ragged) {
-      if constexpr (SPARSE) t = tile_of(t);
+    bool masked;
+    int nvalid;  // valid keys of the tile visited at t
+    if constexpr (SPARSE) {
+      nvalid = kBlockN;
+      if (t < ntiles) {
+        const int e = tile_lds[t];
+        nvalid = a.cube.on ? cube_len_of_flags(a.cube, e >> 13) : kv_len - (e & 0x1fff) * kBlockN;
+      }
+      masked = nvalid < kBlockN;
+    } else {
+      masked = t == ntiles - 1 && ragged;
+      nvalid = kv_len - t * kBlockN;
+    }
+    if (masked) {
       // the lane's first key offset past the valid keys of the tile; opaque, so the
       // compiler neither executes this block unconditionally with selects nor keeps
       // the 32 comparisons of the last tile alive across the loop (64 scalar
       // registers, which it then spills)
-      int lim = kv_len - t * kBlockN - kblk0 * 32 - 4 * hl;
+      int lim = nvalid - kblk0 * 32 - 4 * hl;
       asm volatile("" : "+v"(lim));
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
@@ -780,6 +809,19 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
     }
   };
 
+  // Block-sparse cube tiles: a cube may hold 32 tokens or fewer, so the key half of a
+  // tile that one wave of a query block takes can be empty. Both waves then use the
+  // maximum over the whole tile (their two halves) as the reference.
+  auto share_ref = [&](float (&m)[QB]) {
+    if constexpr (SPARSE) {
+      if (a.cube.on) {
+        if (hl == 0) ref_lds[wave * 32 + l32] = m[0];
+        __syncthreads();
+        m[0] = fmaxf(m[0], ref_lds[(wave ^ 1) * 32 + l32]);
+      }
+    }
+  };
+
   // reference of the weights in o and l_run
   float mfin[QB];
   if constexpr (RETRY) {
@@ -795,6 +837,7 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
     // ---- reference maximum from the first key tile
     prologue();
     tile_max(s_a, c_a, mfin);
+    share_ref(mfin);
     main_pass(mfin);
     // ---- rare path: some weight left the float16 range (a later key scored far
     // above the first tile's maximum) or the inputs were not finite.
@@ -807,6 +850,7 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
       __syncthreads();
       if (wg_retry) {
         exact_max(mfin);
+        share_ref(mfin);
         prologue();
         main_pass(mfin);
       }
@@ -953,7 +997,7 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
 template <int D, int QB, int WAVES, int NST, bool ROPE, bool QK8, bool SPARSE = false>
 hipError_t launch_fwd_t(AttnArgs a, hipStream_t s) {
   using C = FwdCfg<D, QB, WAVES, QK8, SPARSE ? 2 : 1>;
-  a.n_qtiles = (a.nq + C::kBlockM - 1) / C::kBlockM;
+  a.n_qtiles = SPARSE && a.cube.on ? a.cube.n : (a.nq + C::kBlockM - 1) / C::kBlockM;
   const int64_t nbh = (int64_t)a.hc * a.batch;
   const int64_t nwg = (int64_t)a.n_qtiles * nbh;
   if (nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidValue;

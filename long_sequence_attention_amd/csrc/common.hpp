@@ -108,6 +108,62 @@ constexpr int kSmallKeys = 1024;
 constexpr int kVsaMaxTiles = 8192;  // key tiles one selection can rank (32 keys per thread of the select kernel)
 constexpr int kVsaMaxKeep = 4096;   // kept tiles per query tile (the attention kernel's LDS list)
 
+// Block-sparse tiles as 4 x 4 x 4 cubes of a (T, H, W) latent grid (token index
+// (t H + y) W + x). Cube j = (ct, cy, cx), numbered with cx fastest, holds the
+// tokens with t / 4 = ct, y / 4 = cy, x / 4 = cx in ascending order; the last cube
+// along a side that is not a multiple of 4 is thinner, so a cube holds 1 to 64
+// tokens. Slot s of a cube (s < its token count) is its s-th token; in the
+// workspace a cube occupies one 64-key tile whose slots past the count are zero.
+constexpr int kCube = 4;
+struct CubeGeom {
+  int32_t on;            // 0: tiles are runs of 64 consecutive tokens
+  int32_t t, h, w;       // grid sides
+  int32_t nct, ncy, ncx; // cubes along each side
+  int32_t n;             // cubes, nct * ncy * ncx (at most kVsaMaxTiles)
+};
+
+struct Cube {
+  int32_t tok0;          // token of the cube's first slot
+  int32_t et, ey, ex;    // extent along t, y and x (1..4)
+  int32_t len;           // tokens, et * ey * ex
+  int32_t flags;         // bit 0/1/2: the last cube along t / y / x
+};
+
+__host__ __device__ __forceinline__ Cube cube_at(const CubeGeom& g, int j) {
+  const int nyx = g.ncy * g.ncx;
+  const int ct = j / nyx;
+  const int r = j - ct * nyx;
+  const int cy = r / g.ncx;
+  const int cx = r - cy * g.ncx;
+  Cube c;
+  const int rt = g.t - kCube * ct, ry = g.h - kCube * cy, rx = g.w - kCube * cx;
+  c.et = rt < kCube ? rt : kCube;
+  c.ey = ry < kCube ? ry : kCube;
+  c.ex = rx < kCube ? rx : kCube;
+  c.len = c.et * c.ey * c.ex;
+  c.tok0 = (kCube * ct * g.h + kCube * cy) * g.w + kCube * cx;
+  c.flags = (ct == g.nct - 1 ? 1 : 0) | (cy == g.ncy - 1 ? 2 : 0) | (cx == g.ncx - 1 ? 4 : 0);
+  return c;
+}
+
+// Token of slot s (< c.len) of cube c: slots run x fastest, then y, then t.
+__host__ __device__ __forceinline__ int cube_token(const CubeGeom& g, const Cube& c, int s) {
+  const int exy = c.ex * c.ey;
+  const int dt = s / exy;
+  const int r = s - dt * exy;
+  const int dy = r / c.ex;
+  const int dx = r - dy * c.ex;
+  return c.tok0 + (dt * g.h + dy) * g.w + dx;
+}
+
+// Token count of a cube from its flags (the extents of the last cubes are fixed).
+__host__ __device__ __forceinline__ int cube_len_of_flags(const CubeGeom& g, int flags) {
+  const int et = (flags & 1) ? g.t - kCube * (g.nct - 1) : kCube;
+  const int ey = (flags & 2) ? g.h - kCube * (g.ncy - 1) : kCube;
+  const int ex = (flags & 4) ? g.w - kCube * (g.ncx - 1) : kCube;
+  return et * ey * ex;
+}
+
 // v is converted to float16 for the weighted sum after scaling by a power of two
 // 2^e per (entry, head), chosen from max |v| over the valid keys so that the
 // largest value lands in [2^14, 2^15): every bfloat16 value within 2^29 of the
@@ -182,6 +238,9 @@ struct AttnArgs {
   int32_t* retry_cnt;
   int32_t* retry_rows;
   int32_t kv_len[kMaxBatch];  // valid keys of each entry
+  // block-sparse tiles as latent-grid cubes: q rows are mapped through the cubes, k is
+  // the cube-ordered copy in the workspace and kv_len counts its slots
+  CubeGeom cube;
 };
 
 struct QuantArgs {
@@ -221,6 +280,9 @@ struct PrepArgs {
   float* vpart;          // [bh][kVParts] partial maxima of |v|
   int32_t* vexp;         // [bh] exponent of the v scaling (written by key tile 0)
   int32_t* retry_cnt;    // [bh][2] retry counters of the attention launch, cleared by key tile 0
+  // latent-grid cubes: key tile j of V^T (and of the k copy in kr) holds cube j's
+  // tokens, n_ktiles = cubes
+  CubeGeom cube;
   int32_t kv_len[kMaxBatch];
 };
 
@@ -231,9 +293,10 @@ struct VsaMeanArgs {
   int64_t batch;    // elements between batch entries
   float* mean;
   int32_t n;        // tokens
-  int32_t tiles;    // ceil(n / 64)
+  int32_t tiles;    // ceil(n / 64), or the cubes
   int32_t hc;
   int32_t bh;       // entries * hc
+  CubeGeom cube;    // on: tile j is cube j
 };
 
 // Coarse scores [bh][tq][tk] of the tile means, and the kept tiles [bh][tq][keep].

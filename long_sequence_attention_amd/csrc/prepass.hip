@@ -73,7 +73,15 @@ __global__ void __launch_bounds__(256) prepare_kernel(PrepArgs a) {
   const int tid = threadIdx.x;
   const int kv_len = a.kv_len[bat];
   // tiles past this entry's keys are never read by the attention kernel
-  if (tile * kBlockN >= kv_len) return;
+  if (!a.cube.on && tile * kBlockN >= kv_len) return;
+  // latent-grid cubes: this tile holds cube `tile`, slot kl its kl-th token
+  Cube cb{};
+  if (a.cube.on) cb = cube_at(a.cube, tile);
+  auto key_of = [&](int kl) -> int {
+    if (a.cube.on) return kl < cb.len ? cube_token(a.cube, cb, kl) : -1;
+    const int key = tile * kBlockN + kl;
+    return key < kv_len ? key : -1;
+  };
   const __bf16* vsrc = a.v + bat * a.kv_batch + (int64_t)head * a.kv_head;
   // the scaling of this (entry, head): every wave combines the partial maxima
   static_assert(kVParts == kWave, "one partial maximum per lane");
@@ -94,9 +102,9 @@ __global__ void __launch_bounds__(256) prepare_kernel(PrepArgs a) {
     const int qd = i * 256 + tid;
     const int kl = qd / kChunks;
     const int ch = qd % kChunks;
-    const int key = tile * kBlockN + kl;
+    const int key = key_of(kl);
     bf16x8 v = bf16x8{};
-    if (key < kv_len) v = *reinterpret_cast<const bf16x8*>(vsrc + (int64_t)key * a.kv_row + ch * 8);
+    if (key >= 0) v = *reinterpret_cast<const bf16x8*>(vsrc + (int64_t)key * a.kv_row + ch * 8);
     const int pos = vt_position(kl);
 #pragma unroll
     for (int e = 0; e < 8; ++e) tr[(ch * 8 + e) * kPad + pos] = (_Float16)__builtin_amdgcn_ldexpf((float)v[e], vsh);
@@ -110,6 +118,23 @@ __global__ void __launch_bounds__(256) prepare_kernel(PrepArgs a) {
     const int ch = qd & 7;
     *reinterpret_cast<u32x4*>(dst + row * kBlockN + ch * 8) =
         *reinterpret_cast<const u32x4*>(&tr[row * kPad + ch * 8]);
+  }
+
+  if (!ROPE && a.cube.on) {
+    // k in cube order: slot kl of tile `tile` holds the cube's kl-th key (zero past
+    // its token count; the attention kernel masks those scores)
+    const __bf16* ksrc = a.k + bat * a.kv_batch + (int64_t)head * a.kv_head;
+    __bf16* kdst = a.kr + (int64_t)bh * a.kr_head + (int64_t)tile * kBlockN * D;
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int qd = i * 256 + tid;
+      const int kl = qd / kChunks;
+      const int ch = qd % kChunks;
+      const int key = key_of(kl);
+      bf16x8 v = bf16x8{};
+      if (key >= 0) v = *reinterpret_cast<const bf16x8*>(ksrc + (int64_t)key * a.kv_row + ch * 8);
+      *reinterpret_cast<bf16x8*>(kdst + kl * D + ch * 8) = v;
+    }
   }
 
   if constexpr (ROPE) {
@@ -247,6 +272,7 @@ hipError_t launch_prepare(const PrepArgs& a, int head_dim, bool rope_k, hipStrea
   if (a.n_ktiles <= 0 || a.hc <= 0 || a.batch <= 0 || a.batch > kMaxBatch || (int64_t)a.hc * a.batch > 65535 ||
       !a.vpart || !a.vexp)
     return hipErrorInvalidValue;
+  if (a.cube.on && (rope_k || !a.kr || a.n_ktiles != a.cube.n)) return hipErrorInvalidValue;
   if (head_dim == 128) return rope_k ? launch_prepare_t<128, true>(a, s) : launch_prepare_t<128, false>(a, s);
   if (head_dim == 64) return rope_k ? launch_prepare_t<64, true>(a, s) : launch_prepare_t<64, false>(a, s);
   return hipErrorInvalidValue;

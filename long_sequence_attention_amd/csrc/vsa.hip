@@ -1,6 +1,7 @@
 // Tile selection of block-sparse attention over 64-token tiles (the coarse stage
 // of video sparse attention): tile means of q and k, coarse scores between the
-// means, and per query tile the key tiles of highest score.
+// means, and per query tile the key tiles of highest score. A tile is a run of 64
+// consecutive tokens, or a 4 x 4 x 4 cube of the latent grid (CubeGeom).
 //
 // The selection is an integer decided by floating point, so its arithmetic is
 // fixed: means are float32 sums in token order divided by the token count,
@@ -13,7 +14,8 @@
 namespace vdit {
 namespace {
 
-// One wave per (tile, entry * head): lane l sums dimensions [E l, E l + E).
+// One wave per (tile, entry * head): lane l sums dimensions [E l, E l + E) over the
+// tile's tokens in ascending order.
 template <int D>
 __global__ void __launch_bounds__(64) vsa_mean_kernel(VsaMeanArgs a) {
   constexpr int E = D / 64;
@@ -21,12 +23,37 @@ __global__ void __launch_bounds__(64) vsa_mean_kernel(VsaMeanArgs a) {
   const int bh = blockIdx.y;
   const int bat = bh / a.hc;
   const int head = bh - bat * a.hc;
-  const int r0 = t * 64;
-  const int cnt = min(64, a.n - r0);
-  const __bf16* p = a.x + bat * a.batch + (int64_t)head * D + (int64_t)r0 * a.row + threadIdx.x * E;
   float s[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) s[e] = 0.0f;
+  int cnt;
+  if (a.cube.on) {
+    // cube t: its tokens in ascending order, 16 loads in flight, the sums in order
+    const Cube cb = cube_at(a.cube, t);
+    cnt = cb.len;
+    const __bf16* base = a.x + bat * a.batch + (int64_t)head * D + threadIdx.x * E;
+    for (int r0 = 0; r0 < cnt; r0 += 16) {
+      __bf16 x[16][E];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int tok = r0 + r < cnt ? cube_token(a.cube, cb, r0 + r) : 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) x[r][e] = base[(int64_t)tok * a.row + e];
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (r0 + r < cnt)
+#pragma unroll
+          for (int e = 0; e < E; ++e) s[e] = __fadd_rn(s[e], (float)x[r][e]);
+    }
+    float* m = a.mean + ((int64_t)bh * a.tiles + t) * D + threadIdx.x * E;
+#pragma unroll
+    for (int e = 0; e < E; ++e) m[e] = __fdiv_rn(s[e], (float)cnt);
+    return;
+  }
+  const int r0 = t * 64;
+  cnt = min(64, a.n - r0);
+  const __bf16* p = a.x + bat * a.batch + (int64_t)head * D + (int64_t)r0 * a.row + threadIdx.x * E;
   if (cnt == 64) {
     // full tile: all 64 loads in flight in groups of 16, the sums still in token order
 #pragma unroll
@@ -216,6 +243,7 @@ __global__ void __launch_bounds__(kSelThreads) vsa_select_kernel(VsaSelectArgs a
 
 hipError_t launch_vsa_means(const VsaMeanArgs& a, int head_dim, hipStream_t s) {
   if (a.tiles <= 0 || a.bh <= 0 || a.bh > 65535) return hipErrorInvalidValue;
+  if (a.cube.on && (a.tiles != a.cube.n || (int64_t)a.cube.t * a.cube.h * a.cube.w != a.n)) return hipErrorInvalidValue;
   const dim3 grid((unsigned)a.tiles, (unsigned)a.bh);
   if (head_dim == 128)
     hipLaunchKernelGGL(vsa_mean_kernel<128>, grid, dim3(64), 0, s, a);

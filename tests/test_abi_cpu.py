@@ -111,6 +111,10 @@ ROPE = {"grid": (4, 32, 32), "dims": (44, 42, 42), "base": 10000.0}
     (dict(qk_int8=True, head_dim=64), UNSUPPORTED),
     (dict(qk_int8=True, rope=ROPE), UNSUPPORTED),
     (dict(qk_int8=True, nq=64, nk=262145), UNSUPPORTED),
+    (dict(vsa_cubes=(4, 32, 31)), INVALID),                  # the grid does not hold nq tokens
+    (dict(vsa_cubes=(0, 64, 64)), INVALID),
+    (dict(vsa_cubes=(4, 32, 32), nk=2048), INVALID),         # nq != nk
+    (dict(vsa_cubes=(8, 256, 260), nq=532480, nk=532480), UNSUPPORTED),  # 8320 cubes > 8192
     # a 64-key tile's row offsets must fit 32-bit byte offsets: 64 * token stride * 2 < 2^31
     (dict(nq=64, nk=64, heads_total=131072, head_count=1), UNSUPPORTED),
     (dict(nq=64, nk=64, heads_total=43691, head_count=1, layout="N3HD"), UNSUPPORTED),
