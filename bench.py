@@ -14,7 +14,8 @@ lengths 512 and 226; and the same workload with q.k on int8 per-block codes
 (``qk_int8_*``: nominal TFLOP/s, and the fraction of a roofline that prices q.k
 at the int8 MFMA peak and the weighted sum at the float16 peak); and block-sparse
 attention over 64-token tiles at sparsity 0.8 (``vsa_*``: selection and fine-stage
-times, TFLOP/s over the kept keys, speed-up of the whole call over the dense step);
+times, TFLOP/s over the kept keys, speed-up of the whole call over the dense step),
+and the same with tiles that are 4x4x4 cubes of the latent grid (``vsa_cubes_*``);
 and the other workloads of the hot path, each timed alone: N=256 H=2 d=64 (latency),
 N=4096 H=10, text cross-attention (75600 queries, 40 heads, 512 keys, key lengths 512 and a
 seeded one), packed [N,3,40,128] with 3D RoPE at N=131072.
@@ -40,7 +41,8 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-N_TOK = 21 * 45 * 80
+GRID = (21, 45, 80)
+N_TOK = GRID[0] * GRID[1] * GRID[2]
 HEADS_TOTAL, HEAD_BEGIN, HEAD_COUNT, D = 40, 0, 10, 128
 SEED = 1003
 PEAK_TFLOPS = 2500.0          # MI355X dense bf16 / fp16 MFMA
@@ -347,6 +349,30 @@ def main() -> int:
     batched["vsa_frac_of_peak"] = round(vsa_flops / (att_ms * 1e-3) / 1e12 / PEAK_TFLOPS, 4)
     batched["vsa_speedup_vs_dense"] = round(step_ms / fwd_ms, 2)
     del av, wsv, tiles, ov
+
+    # the same with tiles that are 4x4x4 cubes of the latent grid: 6 x 12 x 20 = 1440
+    # cubes, the last frame and the last row of cubes one token thin (16 or 4 tokens)
+    ac = vd.Attention(N_TOK, N_TOK, HEADS_TOTAL, D, head_begin=HEAD_BEGIN, head_count=HEAD_COUNT, vsa_cubes=GRID)
+    keep = ac.vsa_keep(0.8)
+    wsc = ac.new_vsa_workspace(keep, dev)
+    tiles = torch.empty(ac.tiles_shape(keep), dtype=torch.int32, device=dev)
+    oc = torch.empty(ac.out_shape, dtype=torch.bfloat16, device=dev)
+    sel_ms = time_calls(lambda: ac.vsa_select(qd, kd, keep=keep, tiles=tiles, workspace=wsc), 5)
+    att_ms = time_calls(lambda: ac.vsa_attend(qd, kd, vdd, tiles=tiles, out=oc, workspace=wsc), 5)
+    fwd_ms = time_calls(lambda: ac.vsa_forward(qd, kd, vdd, keep=keep, out=oc, workspace=wsc), 5)
+    ext = [np.minimum(4, g - 4 * np.arange((g + 3) // 4)) for g in GRID]       # cube extents per side
+    lens = (ext[0][:, None, None] * ext[1][None, :, None] * ext[2][None, None, :]).reshape(-1)
+    keys = lens[tiles.cpu().numpy()].sum(axis=-1)                              # [heads, query cubes]
+    cube_flops = 4.0 * D * float((keys * lens[None, :]).sum())
+    batched["vsa_cubes_keep_tiles"] = keep
+    batched["vsa_cubes_key_tiles"] = ac.k_tiles
+    batched["vsa_cubes_select_ms"] = round(sel_ms, 4)
+    batched["vsa_cubes_attend_ms"] = round(att_ms, 3)
+    batched["vsa_cubes_fwd_ms"] = round(fwd_ms, 3)
+    batched["vsa_cubes_TFLOPs"] = round(cube_flops / (att_ms * 1e-3) / 1e12, 1)
+    batched["vsa_cubes_frac_of_peak"] = round(cube_flops / (att_ms * 1e-3) / 1e12 / PEAK_TFLOPS, 4)
+    batched["vsa_cubes_speedup_vs_dense"] = round(step_ms / fwd_ms, 2)
+    del ac, wsc, tiles, oc
 
     # the other workloads of the hot path, each timed alone (prepare + attend); inputs
     # are slices of this run's tensors, or fresh N(0, sigma^2) bfloat16 draws on the GPU
