@@ -67,6 +67,12 @@ int main() {
       {"rope base 0", [](vdit_attn_desc_t& d) {
          d.use_rope = 1; d.grid_t = 3; d.grid_h = 10; d.grid_w = 10;
          d.rope_dim_t = 44; d.rope_dim_h = 42; d.rope_dim_w = 42; d.rope_base = 0.0; }, VDIT_ERR_INVALID_ARG},
+      {"cube grid", [](vdit_attn_desc_t& d) { d.vsa_cubes = 1; d.grid_t = 3; d.grid_h = 10; d.grid_w = 11; },
+       VDIT_ERR_INVALID_ARG},
+      {"cube flag 2", [](vdit_attn_desc_t& d) { d.vsa_cubes = 2; d.grid_t = 3; d.grid_h = 10; d.grid_w = 10; },
+       VDIT_ERR_INVALID_ARG},
+      {"cube count", [](vdit_attn_desc_t& d) {
+         d.nq = d.nk = 532480; d.vsa_cubes = 1; d.grid_t = 8; d.grid_h = 256; d.grid_w = 260; }, VDIT_ERR_UNSUPPORTED},
   };
   for (const Bad& x : bads) {
     vdit_attn_desc_t d = good();
