@@ -210,3 +210,27 @@ def test_ulysses_share_n75600_cubes_sparsity_08(dev):
     assert len(rows) >= 4096
     ref, _ = oracle.vsa_reference(q, k, v, head_begin=h0, head_count=hc, rows=rows, tiles=want, grid=grid)
     check(as_f64(out[torch.from_numpy(rows).to(dev)]), ref, f"vsa cubes N={n} ({len(rows)} rows x {hc} heads)")
+
+
+def test_packed_layout_equals_separate(dev):
+    """The packed [N, 3, Ht, d] layout with cube tiles gives the separate layout's bits."""
+    vd = vdm()
+    grid = (5, 6, 9)
+    n, ht, d, keep = 270, 2, 128, 3
+    note(f"vsa cubes packed grid={grid} keep={keep}")
+    qkv = si.normal_bf16((n, 3, ht, d), 4040, si.STREAM_Q)
+    packed = vd.Attention(n, n, ht, d, layout="N3HD", vsa_cubes=grid)
+    sep = vd.Attention(n, n, ht, d, vsa_cubes=grid)
+    both = up(qkv, dev)
+    tp = packed.vsa_select(both, keep=keep)
+    op = packed.vsa_forward(both, keep=keep)
+    q, k, v = (up(np.ascontiguousarray(qkv[:, j]), dev) for j in range(3))
+    ts = sep.vsa_select(q, k, keep=keep)
+    os_ = sep.vsa_forward(q, k, v, keep=keep)
+    torch.cuda.synchronize()
+    assert torch.equal(tp, ts)
+    assert np.array_equal(down(op), down(os_))
+    want = oracle.vsa_select(qkv, layout="N3HD", keep=keep, grid=grid)
+    assert np.array_equal(tp.cpu().numpy(), want)
+    ref, _ = oracle.vsa_reference(qkv, layout="N3HD", tiles=want, grid=grid)
+    check(as_f64(op), ref, "vsa cubes packed")
