@@ -145,6 +145,28 @@ def test_ulysses_share_n75600(dev):
 
 
 @pytest.mark.timeout(900)
+def test_n75600_large_logits_retry_most_rows(dev):
+    # q and k ~ N(0, 3^2): scores have a standard deviation of 9, so for most rows some
+    # key scores more than 16 (log2 units) above the first key tile's maximum and the
+    # float16 weights overflow; those rows go through the retry list at full size
+    n, ht, d = 21 * 45 * 80, 10, 128
+    note(f"N={n} H={ht} d={d}, q and k ~ N(0, 3^2), seed 1007")
+    q = si.normal_bf16((n, ht, d), 1007, si.STREAM_Q, 3.0)
+    k = si.normal_bf16((n, ht, d), 1007, si.STREAM_K, 3.0)
+    v = si.normal_bf16((n, ht, d), 1007, si.STREAM_V, 1.0)
+    # the inputs do reach the retry: rows whose best key beats the first tile's best by
+    # more than 16 in log2 units (head 0, 256 rows, float64)
+    qs = oracle.bf16_bits_to_f64(q[:256, 0])
+    s = qs @ oracle.bf16_bits_to_f64(k[:, 0]).T / np.sqrt(d) * np.log2(np.e)
+    assert np.mean(s.max(axis=1) - s[:, :64].max(axis=1) > 16.0) > 0.5
+    out = run_nhd(dev, q, k, v)
+    rows = si.sample_rows(n, 4096, 1007, si.tile_edge_rows(n))
+    got = as_f64(out[torch.from_numpy(rows).to(dev)])
+    ref = oracle.mha_reference(q, k, v, rows=rows)
+    check(got, ref, f"N={n} large logits ({len(rows)} rows x {ht} heads)")
+
+
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("fixed_len", [None, 64, 512])
 def test_text_cross_attention_key_mask(dev, fixed_len):
     nq, nk = 75600, 512
