@@ -80,15 +80,16 @@ def test_dense_attention_graph_replay(dev, masked):
     replay_checks(g, out, eager, q, q_new)
 
 
-def test_block_sparse_graph_replay(dev):
+@pytest.mark.parametrize("cubes", [None, (5, 9, 57)])
+def test_block_sparse_graph_replay(dev, cubes):
     import long_sequence_attention_amd as vd
-    n, ht, d = 64 * 40 + 9, 2, 128
-    note(f"graph replay block-sparse n={n}")
+    n, ht, d = (64 * 40 + 9 if cubes is None else int(np.prod(cubes))), 2, 128
+    note(f"graph replay block-sparse n={n} cubes={cubes}")
     q = up(si.normal_bf16((n, ht, d), 4410, si.STREAM_Q), dev)
     k = up(si.normal_bf16((n, ht, d), 4410, si.STREAM_K), dev)
     v = up(si.normal_bf16((n, ht, d), 4410, si.STREAM_V), dev)
     q_new = up(si.normal_bf16((n, ht, d), 4411, si.STREAM_Q), dev)
-    attn = vd.Attention(n, n, ht, d)
+    attn = vd.Attention(n, n, ht, d, vsa_cubes=cubes)
     keep = attn.vsa_keep(0.8)
     out = torch.empty(attn.out_shape, dtype=torch.bfloat16, device=dev)
     ws = attn.new_vsa_workspace(keep, dev)
@@ -121,3 +122,30 @@ def test_resident_cross_attention_graph_replay(dev):
         torch.cuda.synchronize()
         return down(o)
     replay_checks(g, out, eager, q, q_new)
+
+
+def test_retry_list_graph_replay(dev):
+    # q[:, :, 0] = 8 and keys whose first dimension ramps up: most rows overflow the
+    # first tile's reference, so every replay lists rows (the list counters are cleared
+    # by the captured prepare and again by the retry launch) and recomputes them
+    import long_sequence_attention_amd as vd
+    nq, nk, ht, d = 1500, 2600, 2, 128
+    note(f"graph replay with the retry list nq={nq} nk={nk}")
+    q = si.normal_bf16((nq, ht, d), 4430, si.STREAM_Q, 0.25)
+    k = si.normal_bf16((nk, ht, d), 4430, si.STREAM_K, 0.25)
+    v = si.normal_bf16((nk, ht, d), 4430, si.STREAM_V, 1.0)
+    q[:, :, 0] = si.f32_to_bf16_bits(np.full((nq, ht), 8.0, dtype=np.float32))
+    k[:, :, 0] = si.f32_to_bf16_bits(np.broadcast_to((np.arange(nk, dtype=np.float32) / 8.0)[:, None], (nk, ht)))
+    q_new = q.copy()
+    q_new[::3, :, 0] = 0
+    qd, kd, vd_ = up(q, dev), up(k, dev), up(v, dev)
+    attn = vd.Attention(nq, nk, ht, d)
+    out = torch.empty(attn.out_shape, dtype=torch.bfloat16, device=dev)
+    ws = attn.new_workspace(dev)
+    g = capture(lambda: attn.forward(qd, kd, vd_, out=out, workspace=ws))
+
+    def eager():
+        o = attn.forward(qd, kd, vd_)
+        torch.cuda.synchronize()
+        return down(o)
+    replay_checks(g, out, eager, qd, up(q_new, dev))
