@@ -59,21 +59,18 @@ __global__ void __launch_bounds__(256) vrange_kernel(PrepArgs a) {
   if (threadIdx.x == 0) a.vpart[(int64_t)bh * kVParts + part] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
+// One 64-key tile of (entry, head) bh: v scaled by 2^vsh -> float16 V^T tile, and
+// the tile's k in cube order (cube tiles) or rotated (RoPE). Uses `tr` in LDS and
+// one barrier; the caller separates consecutive calls with another.
 template <int D, bool ROPE>
-__global__ void __launch_bounds__(256) prepare_kernel(PrepArgs a) {
+__device__ __forceinline__ void prepare_tile(const PrepArgs& a, int tile, int bh, int vsh, _Float16* tr) {
   constexpr int kChunks = D / 8;
   constexpr int kLoads = kBlockN * kChunks / 256;
-  constexpr int kPad = kBlockN + 8;  // float16 per LDS row: 144 bytes, keeps 16-byte alignment
-  __shared__ __attribute__((aligned(16))) _Float16 tr[D * kPad];
-
-  const int tile = blockIdx.x;
-  const int bh = blockIdx.y;               // batch entry * hc + local head
+  constexpr int kPad = kBlockN + 8;
   const int bat = bh / a.hc;
   const int head = bh - bat * a.hc;
   const int tid = threadIdx.x;
   const int kv_len = a.kv_len[bat];
-  // tiles past this entry's keys are never read by the attention kernel
-  if (!a.cube.on && tile * kBlockN >= kv_len) return;
   // latent-grid cubes: this tile holds cube `tile`, slot kl its kl-th token
   Cube cb{};
   if (a.cube.on) cb = cube_at(a.cube, tile);
@@ -83,19 +80,6 @@ __global__ void __launch_bounds__(256) prepare_kernel(PrepArgs a) {
     return key < kv_len ? key : -1;
   };
   const __bf16* vsrc = a.v + bat * a.kv_batch + (int64_t)head * a.kv_head;
-  // the scaling of this (entry, head): every wave combines the partial maxima
-  static_assert(kVParts == kWave, "one partial maximum per lane");
-  float amax = a.vpart[(int64_t)bh * kVParts + (tid & 63)];
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-  const int vsh = v_scale_exp(amax);
-  if (tile == 0 && tid == 0) {
-    a.vexp[bh] = vsh;
-    if (a.retry_cnt) {
-      a.retry_cnt[2 * bh] = 0;
-      a.retry_cnt[2 * bh + 1] = 0;
-    }
-  }
 
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) {
@@ -155,6 +139,84 @@ __global__ void __launch_bounds__(256) prepare_kernel(PrepArgs a) {
       }
       *reinterpret_cast<bf16x8*>(kdst + (int64_t)key * D + ch * 8) = v;
     }
+  }
+}
+
+template <int D, bool ROPE>
+__global__ void __launch_bounds__(256) prepare_kernel(PrepArgs a) {
+  constexpr int kPad = kBlockN + 8;  // float16 per LDS row: 144 bytes, keeps 16-byte alignment
+  __shared__ __attribute__((aligned(16))) _Float16 tr[D * kPad];
+
+  const int tile = blockIdx.x;
+  const int bh = blockIdx.y;               // batch entry * hc + local head
+  const int bat = bh / a.hc;
+  const int tid = threadIdx.x;
+  // tiles past this entry's keys are never read by the attention kernel
+  if (!a.cube.on && tile * kBlockN >= a.kv_len[bat]) return;
+  // the scaling of this (entry, head): every wave combines the partial maxima
+  static_assert(kVParts == kWave, "one partial maximum per lane");
+  float amax = a.vpart[(int64_t)bh * kVParts + (tid & 63)];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  const int vsh = v_scale_exp(amax);
+  if (tile == 0 && tid == 0) {
+    a.vexp[bh] = vsh;
+    if (a.retry_cnt) {
+      a.retry_cnt[2 * bh] = 0;
+      a.retry_cnt[2 * bh + 1] = 0;
+    }
+  }
+  prepare_tile<D, ROPE>(a, tile, bh, vsh, tr);
+}
+
+// Short key sequences (at most kSmallKeys keys per entry, not cube-tiled): one
+// workgroup per (entry, head) finds max |v| over the valid keys and then prepares
+// every key tile, one launch instead of the range and prepare launches; the values
+// written are the same.
+template <int D, bool ROPE>
+__global__ void __launch_bounds__(256) prepare_short_kernel(PrepArgs a) {
+  constexpr int kChunks = D / 8;
+  constexpr int kPad = kBlockN + 8;
+  __shared__ __attribute__((aligned(16))) _Float16 tr[D * kPad];
+  __shared__ float red[4];
+  const int bh = blockIdx.x;
+  const int bat = bh / a.hc;
+  const int head = bh - bat * a.hc;
+  const int tid = threadIdx.x;
+  const int kv_len = a.kv_len[bat];
+  const __bf16* vsrc = a.v + bat * a.kv_batch + (int64_t)head * a.kv_head;
+  float m = 0.0f;
+  const int total = kv_len * kChunks;
+  for (int c0 = tid; c0 < total; c0 += 4 * 256) {
+    bf16x8 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = c0 + u * 256;
+      v[u] = c < total ? *reinterpret_cast<const bf16x8*>(vsrc + (int64_t)(c / kChunks) * a.kv_row + (c % kChunks) * 8)
+                       : bf16x8{};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf((float)v[u][e]));
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const int vsh = v_scale_exp(amax);
+  if (tid == 0) {
+    a.vexp[bh] = vsh;
+    if (a.retry_cnt) {
+      a.retry_cnt[2 * bh] = 0;
+      a.retry_cnt[2 * bh + 1] = 0;
+    }
+  }
+  const int ntiles = (kv_len + kBlockN - 1) / kBlockN;
+  for (int tile = 0; tile < ntiles; ++tile) {
+    prepare_tile<D, ROPE>(a, tile, bh, vsh, tr);
+    __syncthreads();  // the next tile rewrites tr
   }
 }
 
@@ -261,6 +323,10 @@ __global__ void __launch_bounds__(256) rope_probe_kernel(RopeGeom g, int32_t nq,
 
 template <int D, bool ROPE>
 hipError_t launch_prepare_t(const PrepArgs& a, hipStream_t s) {
+  if (!a.cube.on && a.n_ktiles * kBlockN <= kSmallKeys) {
+    hipLaunchKernelGGL((prepare_short_kernel<D, ROPE>), dim3(a.hc * a.batch), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((vrange_kernel<D>), dim3(kVParts, a.hc * a.batch), dim3(256), 0, s, a);
   hipLaunchKernelGGL((prepare_kernel<D, ROPE>), dim3(a.n_ktiles, a.hc * a.batch), dim3(256), 0, s, a);
   return hipGetLastError();

@@ -592,6 +592,43 @@ def test_value_scale_resident_and_four_stage_kernels(dev, sigma_v):
         check(as_f64(out), oracle.mha_reference(q, k, v), f"v scale {sigma_v:g} nk={nk}", v_scale=sigma_v)
 
 
+@pytest.mark.parametrize("d,rope", [(128, None), (64, None),
+                                    (128, {"grid": (2, 24, 25), "dims": (44, 42, 42), "base": 10000.0})])
+def test_short_key_prepare_equals_two_pass_prepare(dev, d, rope):
+    # up to 1024 keys the range of v and the conversion run in one launch (one
+    # workgroup per head); beyond, two launches. With the keys past 1000 set to zero
+    # (so that max |v| is the same), key length 1000 (one launch) and 1200 (two) must
+    # write the same V^T tiles 0..15, rotated keys and exponents
+    vd = vdm()
+    n, ht = 1200, 3
+    note(f"short-key prepare vs two-pass prepare d={d} rope={rope is not None}")
+    q, k, v = nhd_inputs(n, n, ht, d, 9990 + d, 0.5)
+    v[1000:] = 0
+    if rope is not None:
+        k[1000:] = 0
+    attn = vd.Attention(n, n, ht, d, use_key_mask=True, rope=rope)
+    qd, kd, vd_ = up(q, dev), up(k, dev), up(v, dev)
+    w1 = attn.prepare(qd, kd, vd_, key_len=1000)
+    w2 = attn.prepare(qd, kd, vd_, key_len=1200)
+    torch.cuda.synchronize()
+    lay = workspace_layout(1, ht, n, n, d, rope=rope is not None)
+    per_head = lay["nk_pad"] * d * 2
+    for h in range(ht):
+        a = w1[lay["vt"] + h * per_head:lay["vt"] + h * per_head + 16 * 64 * d * 2]
+        b = w2[lay["vt"] + h * per_head:lay["vt"] + h * per_head + 16 * 64 * d * 2]
+        assert torch.equal(a, b), f"V^T head {h}"
+        if rope is not None:
+            a = w1[lay["kr"] + h * per_head:lay["kr"] + h * per_head + 1000 * d * 2]
+            b = w2[lay["kr"] + h * per_head:lay["kr"] + h * per_head + 1000 * d * 2]
+            assert torch.equal(a, b), f"rotated k head {h}"
+    e1 = w1[lay["vexp"]:lay["vexp"] + ht * 4].view(torch.int32)
+    e2 = w2[lay["vexp"]:lay["vexp"] + ht * 4].view(torch.int32)
+    assert torch.equal(e1, e2)
+    out = attn.attend(qd, kd, vd_, key_len=1000, workspace=w1)
+    torch.cuda.synchronize()
+    check(as_f64(out), oracle.mha_reference(q, k, v, key_len=1000, rope=rope), f"short-key prepare d={d}")
+
+
 def test_value_scale_ignores_masked_keys(dev):
     # the range of v is taken over the valid keys only: huge or non-finite values
     # past the key length change nothing
