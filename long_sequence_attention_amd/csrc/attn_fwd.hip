@@ -1026,6 +1026,22 @@ int device_cus() {
   return n;
 }
 
+// The arguments of batch entry b alone (a batch of one).
+AttnArgs entry_args(const AttnArgs& a, int b) {
+  AttnArgs e = a;
+  e.q = a.q + b * a.q_batch;
+  e.k = a.k + b * a.k_batch;
+  e.vt = a.vt + b * a.vt_batch;
+  e.out = a.out + b * a.out_batch;
+  e.vexp = a.vexp + (int64_t)b * a.hc;
+  e.retry_cnt = a.retry_cnt ? a.retry_cnt + (int64_t)2 * b * a.hc : nullptr;
+  e.retry_rows = a.retry_rows ? a.retry_rows + (int64_t)b * a.hc * a.nq : nullptr;
+  e.batch = 1;
+  for (int i = 0; i < kMaxBatch; ++i) e.kv_len[i] = 0;
+  e.kv_len[0] = a.kv_len[b];
+  return e;
+}
+
 }  // namespace
 
 
@@ -1038,6 +1054,28 @@ hipError_t launch_attn_fwd(const AttnArgs& a, int head_dim, bool rope_q, bool qk
     // the two-stage int8 configuration holds the k scales of short key sequences only
     if (head_dim != 128 || rope_q) return hipErrorInvalidValue;
     return short_keys ? launch_fwd_t<128, 1, 4, 2, false, true>(a, s) : launch_fwd_t<128, 1, 8, 4, false, true>(a, s);
+  }
+  // A batch that mixes key lengths fitting the LDS array with longer ones (e.g. the
+  // two conditionings of guidance with 512 and 226 text tokens): each entry is
+  // launched on its own, so that the short ones take the resident kernel. Both
+  // kernels compute every row the same way, so the results do not change.
+  if (!rope_q && a.batch > 1) {
+    const int rmax = resident_max_keys(head_dim);
+    bool any_short = false, any_long = false;
+    for (int b = 0; b < a.batch; ++b) {
+      if (a.kv_len[b] <= rmax)
+        any_short = true;
+      else
+        any_long = true;
+    }
+    const int cus = device_cus();
+    if (any_short && any_long && cus > 0 && resident_query_tiles(a.nq) * a.hc >= cus) {
+      for (int b = 0; b < a.batch; ++b) {
+        const hipError_t e = launch_attn_fwd(entry_args(a, b), head_dim, rope_q, qk_int8, s);
+        if (e != hipSuccess) return e;
+      }
+      return hipSuccess;
+    }
   }
   // keys and values that fit in LDS, with a query tile for every CU: the resident
   // kernel (one staging of K/V^T per head and workgroup)

@@ -138,3 +138,27 @@ def test_batch_call_errors(dev):
         attn.forward(q[0], k[0], v[0], key_lens=[5, 5])  # missing batch dimension
     # the workspace grows with the batch, as the header lays it out
     assert attn.workspace_bytes == workspace_layout(B, ht, nq, nk, d)["end"]
+
+
+@pytest.mark.parametrize("lens", [(512, 200), (100, 512, 300)])
+def test_batch_mixed_key_lengths_resident_and_streaming(dev, lens):
+    # 16384 queries x 4 heads give every CU a 256-query tile, so entries whose key
+    # length fits the LDS array (<= 256 at d = 128) take the keys-resident kernel and
+    # the others the streaming one, each launched on its own; every entry must still
+    # equal its single call bit for bit
+    vd = vdm()
+    B, nq, nk, ht, d = len(lens), 16384, 512, 4, 128
+    note(f"batch mixed key lengths B={B} nq={nq} key_lens={lens}")
+    es = entries(B, nq, nk, ht, d, 4300)
+    attn = vd.Attention(nq, nk, ht, d, use_key_mask=True, batch=B)
+    out = attn.forward(stack(dev, [e[0] for e in es]), stack(dev, [e[1] for e in es]),
+                       stack(dev, [e[2] for e in es]), key_lens=lens)
+    torch.cuda.synchronize()
+    single = vd.Attention(nq, nk, ht, d, use_key_mask=True)
+    rows = si.sample_rows(nq, 512, 4300, si.tile_edge_rows(nq))
+    for i, (q, k, v) in enumerate(es):
+        o1 = single.forward(up(q, dev), up(k, dev), up(v, dev), key_len=lens[i])
+        torch.cuda.synchronize()
+        assert np.array_equal(down(out[i]), down(o1)), f"entry {i} (key length {lens[i]})"
+        got = as_f64(out[i][torch.from_numpy(rows).to(dev)])
+        check(got, oracle.mha_reference(q, k, v, key_len=lens[i], rows=rows), f"entry {i} L={lens[i]}")
