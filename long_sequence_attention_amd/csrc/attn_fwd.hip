@@ -41,7 +41,7 @@
 // the exact row maximum (a q.k-only pass for the maximum, then the normal pass,
 // where every weight is at most 1). In the block-sparse mode the workgroup
 // recomputes its own rows instead. The row sum is taken from the rounded float16
-// weights (v_dot2), the same values the product uses.
+// weights (added one by one in float32), the same values the product uses.
 #include "common.hpp"
 #include "lds.hpp"
 
@@ -404,7 +404,13 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   // row sums of the rounded weights, one partial per 16-key group of a tile,
   // accumulated over the whole pass and added up at its end
   float lpart[QB][2 * KH];
-  const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+  // Each rounded weight is added to its partial as fma(w, one, l) with w read as a
+  // float16 half of a pair and `one` held in a register, which compiles to
+  // v_fma_mix_f32 (one float32 rounding per addition). A v_dot2 of the pair with
+  // (1, 1) does the same work in half the instructions, but on this chip each
+  // v_dot2 holds up the matrix products about twice as long as two fma_mix do.
+  float one = 1.0f;
+  asm volatile("" : "+v"(one));  // a register operand, not an inline constant
 
   // ---- one iteration's matrix and vector work, scheduled by hand. A tile has
   // kNS score products (k-step j/2, key block j%2) and kNP weight products
@@ -550,7 +556,7 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int s4 = 0; s4 < 2 * KH; ++s4) pf[qb][s4] = __builtin_bit_cast(f16x8, bits[qb][s4]);
   };
-  // O^T += V^T P^T; the row sums of the rounded weights (v_dot2 into lpart) ride
+  // O^T += V^T P^T; the row sums of the rounded weights (fma_mix into lpart) ride
   // along with the products, which have no other vector work
   // with int8 q.k this also converts the integer scores of the next tile to
   // float, two per product
@@ -602,7 +608,8 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
       for (int p = g * kPairs / kNP; p < (g + 1) * kPairs / kNP; ++p)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-          lpart[qb][p >> 2] = __builtin_amdgcn_fdot2(hv[qb][p], ones, lpart[qb][p >> 2], false);
+          lpart[qb][p >> 2] = __builtin_fmaf((float)hv[qb][p][0], one, lpart[qb][p >> 2]);
+          lpart[qb][p >> 2] = __builtin_fmaf((float)hv[qb][p][1], one, lpart[qb][p >> 2]);
           asm volatile("" : "+v"(lpart[qb][p >> 2]));  // keeps the sum in this group
         }
       if constexpr (SPLIT) {

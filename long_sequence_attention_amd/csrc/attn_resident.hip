@@ -181,7 +181,10 @@ __global__ void __launch_bounds__(kResThreads) attn_resident_kernel(AttnArgs a, 
   f32x16 o[C::kDB];
   float l_run;
   float lpart[4];  // row sums per 16-key group of a tile, over the whole pass
-  const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+  // the weights are added one at a time, as the streaming kernel adds them
+  // (fma_mix with a register one), so that both kernels give the same bits
+  float one = 1.0f;
+  asm volatile("" : "+v"(one));
   constexpr int kNS = 2 * C::kDK;     // score products per tile
   constexpr int kNP = 4 * C::kDB;     // weight products per tile
   constexpr int kR = 4;               // LDS fragments read ahead
@@ -283,7 +286,8 @@ __global__ void __launch_bounds__(kResThreads) attn_resident_kernel(AttnArgs a, 
       if (g + kR < kNP) vr[g % kR] = vfrag(T_, g + kR);
 #pragma unroll
       for (int p = g * kPairs / kNP; p < (g + 1) * kPairs / kNP; ++p) {
-        lpart[p >> 2] = __builtin_amdgcn_fdot2(hv[p], ones, lpart[p >> 2], false);
+        lpart[p >> 2] = __builtin_fmaf((float)hv[p][0], one, lpart[p >> 2]);
+        lpart[p >> 2] = __builtin_fmaf((float)hv[p][1], one, lpart[p >> 2]);
         asm volatile("" : "+v"(lpart[p >> 2]));
       }
       __builtin_amdgcn_sched_barrier(0);
