@@ -428,7 +428,6 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   constexpr int kNP = 2 * KH * C::kDB;
   constexpr int kR = 4;
   constexpr int kPairs = 8 * KH;             // float16 pairs of weights per lane
-  constexpr int kPPG = kPairs / kNS;         // pairs per score product
   static_assert(kNS >= kR && kNP >= kR && kPairs % kNS == 0 && kPairs % kNP == 0, "pipeline shape");
   auto kfrag = [&](const char* kl, int j) {
     return *reinterpret_cast<const QFrag*>(kl + (j % KH + kblk0) * 32 * C::kKRow + koff[j / KH]);
@@ -443,9 +442,16 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   // direct loads there, one per product)
   // SPLIT: the weights of a tile are formed half in the score phase (pairs
   // kPairs/2 ..) and half in the product phase before it (pairs 0 .. kPairs/2 - 1,
-  // from the scores just formed), so both phases carry the same vector work.
-  constexpr bool SPLIT = KH == 2 && kNS == kPairs && kNP == kPairs;
+  // from the scores just formed), so that the vector work spreads over both
+  // phases: one pair per two score products with bfloat16 q.k (SPLIT2), one per
+  // score product with int8 q.k, whose score phase has half as many products.
+  constexpr bool SPLIT = KH == 2 && kNP == kPairs && (kNS == kPairs || 2 * kNS == kPairs);
+  constexpr bool SPLIT2 = SPLIT && kNS == kPairs;
   constexpr int kHalf = kPairs / 2;
+  // pairs per score product in the chained form / exp / round pipeline below, and
+  // the first pair of the score phase in those units
+  constexpr int kPPG = SPLIT2 ? 1 : (SPLIT ? kHalf : kPairs) / kNS;
+  constexpr int kG0 = SPLIT ? kHalf / kPPG : 0;
   auto score_phase = [&](const char* k_read, const char* v_read, const f32x16 (&s_cur)[QB][KH],
                          f32x16 (&s_next)[QB][KH], const float (&ccur)[QB], const float (&mref)[QB],
                          f16x8 (&vr)[kR], f16x8 (&pf)[QB][2 * KH], f16x2 (&hv)[QB][kPairs],
@@ -522,7 +528,7 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
     };
 #pragma unroll
     for (int j = 0; j < kR; ++j) kr[j] = kfrag(k_read, j);
-    if constexpr (!SPLIT) form_x(0);
+    if constexpr (!SPLIT2) form_x(kG0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int g = 0; g < kNS; ++g) {
@@ -535,7 +541,7 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
         kr[g % kR] = kfrag(k_read, g + kR);
       else
         vr[g + kR - kNS] = vfrag(v_read, g + kR - kNS);
-      if constexpr (SPLIT) {
+      if constexpr (SPLIT2) {
         static_assert(kNS == 2 * kHalf, "one pair per two score products");
         if (g % 2 == 0) {
           if (g >= 2) round_w(kHalf / kPPG + g / 2 - 1);
@@ -544,13 +550,13 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
           exp_x();
         }
       } else {
-        if (g > 0) round_w(g - 1);
+        if (g > 0) round_w(kG0 + g - 1);
         exp_x();
-        if (g + 1 < kNS) form_x(g + 1);
+        if (g + 1 < kNS) form_x(kG0 + g + 1);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    round_w(SPLIT ? kHalf / kPPG + kNS / 2 - 1 : kNS - 1);
+    round_w(SPLIT2 ? kHalf / kPPG + kNS / 2 - 1 : kG0 + kNS - 1);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
