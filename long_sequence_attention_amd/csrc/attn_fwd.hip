@@ -401,9 +401,11 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
   // O^T accumulators and row sums of the weights
   f32x16 o[QB][C::kDB];
   float l_run[QB];
-  // row sums of the rounded weights, one partial per 16-key group of a tile,
-  // accumulated over the whole pass and added up at its end
-  float lpart[QB][2 * KH];
+  // row sums of the rounded weights in eight partials, indexed by (pair index mod 4,
+  // half of the pair), accumulated over the whole pass and added up at its end: the
+  // two halves of a pair and consecutive pairs go to different partials, so no
+  // addition waits on the one before it
+  float lpart[QB][4][2];
   // Each rounded weight is added to its partial as fma(w, one, l) with w read as a
   // float16 half of a pair and `one` held in a register, which compiles to
   // v_fma_mix_f32 (one float32 rounding per addition). A v_dot2 of the pair with
@@ -614,9 +616,11 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
       for (int p = g * kPairs / kNP; p < (g + 1) * kPairs / kNP; ++p)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-          lpart[qb][p >> 2] = __builtin_fmaf((float)hv[qb][p][0], one, lpart[qb][p >> 2]);
-          lpart[qb][p >> 2] = __builtin_fmaf((float)hv[qb][p][1], one, lpart[qb][p >> 2]);
-          asm volatile("" : "+v"(lpart[qb][p >> 2]));  // keeps the sum in this group
+          float& l0 = lpart[qb][p & 3][0];
+          float& l1 = lpart[qb][p & 3][1];
+          l0 = __builtin_fmaf((float)hv[qb][p][0], one, l0);
+          l1 = __builtin_fmaf((float)hv[qb][p][1], one, l1);
+          asm volatile("" : "+v"(l0), "+v"(l1));  // keeps the sums in this group
         }
       if constexpr (SPLIT) {
         static_assert(kNP == 2 * kHalf, "one pair per two weight products");
@@ -765,7 +769,7 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
-      for (int s4 = 0; s4 < 2 * KH; ++s4) lpart[qb][s4] = 0.0f;
+      for (int i = 0; i < 4; ++i) lpart[qb][i][0] = lpart[qb][i][1] = 0.0f;
 #pragma unroll
       for (int db = 0; db < C::kDB; ++db) o[qb][db] = f32x16{};
     }
@@ -789,10 +793,9 @@ __global__ void __launch_bounds__(WAVES * 64) attn_fwd_kernel(AttnArgs a) {
     barrier_only();
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      if constexpr (KH == 2)
-        l_run[qb] = (lpart[qb][0] + lpart[qb][1]) + (lpart[qb][2] + lpart[qb][3]);
-      else
-        l_run[qb] = lpart[qb][0] + lpart[qb][1];
+      const float q0 = lpart[qb][0][0] + lpart[qb][0][1], q1 = lpart[qb][1][0] + lpart[qb][1][1];
+      const float q2 = lpart[qb][2][0] + lpart[qb][2][1], q3 = lpart[qb][3][0] + lpart[qb][3][1];
+      l_run[qb] = (q0 + q1) + (q2 + q3);
     }
   };
 

@@ -180,7 +180,7 @@ __global__ void __launch_bounds__(kResThreads) attn_resident_kernel(AttnArgs a, 
 
   f32x16 o[C::kDB];
   float l_run;
-  float lpart[4];  // row sums per 16-key group of a tile, over the whole pass
+  float lpart[4][2];  // row sums by (pair index mod 4, half), over the whole pass
   // the weights are added one at a time, as the streaming kernel adds them
   // (fma_mix with a register one), so that both kernels give the same bits
   float one = 1.0f;
@@ -286,9 +286,11 @@ __global__ void __launch_bounds__(kResThreads) attn_resident_kernel(AttnArgs a, 
       if (g + kR < kNP) vr[g % kR] = vfrag(T_, g + kR);
 #pragma unroll
       for (int p = g * kPairs / kNP; p < (g + 1) * kPairs / kNP; ++p) {
-        lpart[p >> 2] = __builtin_fmaf((float)hv[p][0], one, lpart[p >> 2]);
-        lpart[p >> 2] = __builtin_fmaf((float)hv[p][1], one, lpart[p >> 2]);
-        asm volatile("" : "+v"(lpart[p >> 2]));
+        float& l0 = lpart[p & 3][0];
+        float& l1 = lpart[p & 3][1];
+        l0 = __builtin_fmaf((float)hv[p][0], one, l0);
+        l1 = __builtin_fmaf((float)hv[p][1], one, l1);
+        asm volatile("" : "+v"(l0), "+v"(l1));
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -303,7 +305,7 @@ __global__ void __launch_bounds__(kResThreads) attn_resident_kernel(AttnArgs a, 
   f32x16 s[2][2];
   auto main_pass = [&](float mref, const __bf16* qnext) {
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) lpart[s4] = 0.0f;
+    for (int i = 0; i < 4; ++i) lpart[i][0] = lpart[i][1] = 0.0f;
 #pragma unroll
     for (int db = 0; db < C::kDB; ++db) o[db] = f32x16{};
     const int last_scores = ntiles == C::kMaxTiles ? ntiles - 2 : ntiles - 1;
@@ -324,7 +326,9 @@ __global__ void __launch_bounds__(kResThreads) attn_resident_kernel(AttnArgs a, 
         product_phase(T_, vr, pf, hv);
       }
     });
-    l_run = (lpart[0] + lpart[1]) + (lpart[2] + lpart[3]);
+    const float q0 = lpart[0][0] + lpart[0][1], q1 = lpart[1][0] + lpart[1][1];
+    const float q2 = lpart[2][0] + lpart[2][1], q3 = lpart[3][0] + lpart[3][1];
+    l_run = (q0 + q1) + (q2 + q3);
   };
 
   const std::integral_constant<int, 0> tile0{};
