@@ -81,17 +81,28 @@ __device__ __forceinline__ void prepare_tile(const PrepArgs& a, int tile, int bh
   };
   const __bf16* vsrc = a.v + bat * a.kv_batch + (int64_t)head * a.kv_head;
 
+  // thread: kLoads consecutive keys (one 16-byte chunk of each), so that each of
+  // its dimensions goes to LDS as one write of kLoads float16 (consecutive keys stay
+  // adjacent under vt_position) instead of kLoads 2-byte writes
+  {
+    static_assert(kLoads == 2 || kLoads == 4, "keys per thread");
+    typedef _Float16 f16xg __attribute__((ext_vector_type(kLoads)));
+    const int kg = tid / kChunks;
+    const int ch = tid % kChunks;
+    bf16x8 v[kLoads];
 #pragma unroll
-  for (int i = 0; i < kLoads; ++i) {
-    const int qd = i * 256 + tid;
-    const int kl = qd / kChunks;
-    const int ch = qd % kChunks;
-    const int key = key_of(kl);
-    bf16x8 v = bf16x8{};
-    if (key >= 0) v = *reinterpret_cast<const bf16x8*>(vsrc + (int64_t)key * a.kv_row + ch * 8);
-    const int pos = vt_position(kl);
+    for (int j = 0; j < kLoads; ++j) {
+      const int key = key_of(kg * kLoads + j);
+      v[j] = key >= 0 ? *reinterpret_cast<const bf16x8*>(vsrc + (int64_t)key * a.kv_row + ch * 8) : bf16x8{};
+    }
+    const int pos = vt_position(kg * kLoads);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) tr[(ch * 8 + e) * kPad + pos] = (_Float16)__builtin_amdgcn_ldexpf((float)v[e], vsh);
+    for (int e = 0; e < 8; ++e) {
+      f16xg w;
+#pragma unroll
+      for (int j = 0; j < kLoads; ++j) w[j] = (_Float16)__builtin_amdgcn_ldexpf((float)v[j][e], vsh);
+      *reinterpret_cast<f16xg*>(&tr[(ch * 8 + e) * kPad + pos]) = w;
+    }
   }
   __syncthreads();
   _Float16* dst = a.vt + (int64_t)bh * a.vt_head + (int64_t)tile * (D * kBlockN);
